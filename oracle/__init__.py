@@ -1,0 +1,67 @@
+"""CPU oracle for sharded paged decode attention (test infrastructure).
+
+This package is test infrastructure only. It is imported by the tests, by
+``__graft_entry__.smoke()`` and by the CPU-baseline leg of ``bench.py``; the
+library and its Python binding never import or call it.
+
+It computes, in float64 with NumPy, exactly what the pages define:
+
+* interleaved block ownership (block j belongs to shard j mod D) and the
+  global-to-local block-table remap -- "vLLM长序列推理优化：DCP切分KV Cache原理与实战",
+  sections 2.2 and 3.2;
+* single-token softmax attention over a paged cache, unsharded, with GQA
+  head sharing and absorbed-MLA latent rows -- "Efficient Decode Context
+  Parallelism with vLLM for Long Context Workloads", section A2 (Compute step);
+* per-shard partial outputs with their log-sum-exp and the LSE merge
+  O = sum_i exp(LSE_i) / sum_j exp(LSE_j) * O_i -- same page, summary
+  section (merge equation) and A2 (AllGather + ReduceScatter step);
+* the equivalent (m, l) max/sum rescale merge -- "vLLM长序列推理优化", section 2.3.
+
+No blocking, fusion or reordering is added beyond those definitions. Every
+function is pinned by the CPU tests to closed forms, brute force, library
+routines or the pages' worked examples; none is marked "parity unpinned".
+"""
+from .codecs import bf16_to_f64, e4m3_to_f64
+from .paged import (
+    blocks_of,
+    gather_rows,
+    local_lengths,
+    owner_of_block,
+    local_index_of_block,
+    remap_block_table,
+    shard_blocks,
+    tokens_in_block,
+)
+from .attention import (
+    attend,
+    decode_reference,
+    lse_merge,
+    ml_merge,
+    ml_partials,
+    query,
+    sequence_kv,
+    shard_partials,
+    shard_positions,
+)
+
+__all__ = [
+    "bf16_to_f64",
+    "e4m3_to_f64",
+    "blocks_of",
+    "gather_rows",
+    "local_lengths",
+    "owner_of_block",
+    "local_index_of_block",
+    "remap_block_table",
+    "shard_blocks",
+    "tokens_in_block",
+    "attend",
+    "decode_reference",
+    "lse_merge",
+    "ml_merge",
+    "ml_partials",
+    "query",
+    "sequence_kv",
+    "shard_partials",
+    "shard_positions",
+]

@@ -1,0 +1,85 @@
+"""Paged-cache bookkeeping: block ownership, remap and gathers (test infrastructure).
+
+Source: "vLLM长序列推理优化：DCP切分KV Cache原理与实战".
+  * Section 2.2: with D shards, shard i owns the blocks whose index satisfies
+    block_idx % D == i (interleaved, not contiguous).
+  * Section 3.2: the block table keeps global logical indices and is remapped
+    to local indices per shard; global block 4 is local block 1 on shard 0
+    because shard 0 holds global blocks 0, 4, 8, ... with local indices
+    counting from 0.
+The block index that is interleaved is the *logical* index of a block within
+its sequence (position t lives in logical block t // block_size at slot
+t % block_size). The last block of a sequence may be partly filled; it
+belongs to the shard that owns its index like any other block.
+"""
+import numpy as np
+
+
+def owner_of_block(j: int, num_shards: int) -> int:
+    """Shard owning logical block j (section 2.2: block_idx % D)."""
+    return j % num_shards
+
+
+def local_index_of_block(j: int, num_shards: int) -> int:
+    """Position of logical block j in its owner's local table (section 3.2)."""
+    return j // num_shards
+
+
+def blocks_of(seq_len: int, block_size: int) -> int:
+    """Number of logical blocks a sequence of seq_len tokens occupies."""
+    return -(-int(seq_len) // int(block_size))
+
+
+def tokens_in_block(j: int, seq_len: int, block_size: int) -> int:
+    """Valid tokens in logical block j of a sequence of seq_len tokens."""
+    return max(0, min(block_size, seq_len - j * block_size))
+
+
+def shard_blocks(seq_len: int, block_size: int, num_shards: int, shard: int) -> list:
+    """Logical blocks of one sequence that ``shard`` owns, in local order."""
+    return [j for j in range(blocks_of(seq_len, block_size))
+            if owner_of_block(j, num_shards) == shard]
+
+
+def local_lengths(seq_len: int, block_size: int, num_shards: int) -> list:
+    """Tokens each shard holds for one sequence, by counting its blocks."""
+    out = [0] * num_shards
+    for j in range(blocks_of(seq_len, block_size)):
+        out[owner_of_block(j, num_shards)] += tokens_in_block(j, seq_len, block_size)
+    return out
+
+
+def remap_block_table(block_table, seq_lens, block_size: int, num_shards: int):
+    """Global block table -> per-shard local tables (section 3.2).
+
+    block_table: int32 [B, max_blocks] of physical block ids (logical j -> id).
+    Returns (local_table int32 [D, B, ceil(max_blocks / D)] padded with -1,
+             local_lens  int32 [D, B]).
+    Entry [r, b, i] is the physical id of the logical block j with
+    j % D == r and j // D == i.
+    """
+    table = np.asarray(block_table)
+    lens = np.asarray(seq_lens)
+    batch, max_blocks = table.shape
+    width = -(-max_blocks // num_shards)
+    local = np.full((num_shards, batch, width), -1, dtype=np.int32)
+    local_len = np.zeros((num_shards, batch), dtype=np.int32)
+    for b in range(batch):
+        n = min(blocks_of(lens[b], block_size), max_blocks)
+        for j in range(n):
+            r = owner_of_block(j, num_shards)
+            i = local_index_of_block(j, num_shards)
+            local[r, b, i] = table[b, j]
+            local_len[r, b] += tokens_in_block(j, int(lens[b]), block_size)
+    return local, local_len
+
+
+def gather_rows(cache, table_row, positions, block_size: int):
+    """Rows cache[table_row[t // bs], t % bs] for every token position t.
+
+    ``cache`` is indexed [physical block, slot, ...]; the result keeps the
+    trailing dimensions and lists rows in the order of ``positions``.
+    """
+    pos = np.asarray(positions, dtype=np.int64)
+    phys = np.asarray(table_row, dtype=np.int64)[pos // block_size]
+    return cache[phys, pos % block_size]

@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of sharded paged decode attention on one MI355X.
+
+Default workload (mla_bf16_b64_bimodal): absorbed-MLA decode with a bf16
+latent cache, batch 64, 64 query heads over a 576-wide latent (value = first
+512 columns), block size 64, D = 8 interleaved shards, context lengths drawn as
+stratified quantiles of the agentic-trace statistics (median ~67K, 53 % above
+64K, ~8 % above 128K, ~3 % above 256K; sum 5,065,388 tokens, max 769,505).
+
+One step = one dcp_decode_all_shards call over the whole batch: work plan,
+attention over all D shards, and the LSE merge -- one decode token per
+sequence through one attention layer, inputs already resident in HBM.
+
+Prints one JSON line. `value` is KV GB/s: bytes of cached latent rows the step
+must read (sum of lengths x 1152 B) divided by the wall time of a step.
+`roofline.achieved` divides the same bytes by the attention kernel's own
+average duration, measured with HIP events recorded on its stream around
+every timed launch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = ROOT / "profiles"
+KERNEL_SOURCES = ["mla.hip", "gqa.hip", "dcp_internal.hpp"]
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update((ROOT / "decode_attention_sequence_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters(workload: str):
+    """HBM bytes per attention launch from committed counter runs, if current."""
+    path = PROFILES / f"{workload}_hbm_traffic.json"
+    if not path.exists():
+        return None
+    rec = json.loads(path.read_text())
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None  # the kernel changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, o_gpu, lse_gpu, budget_s: float):
+    """Time the fp64 oracle on a stratified sample of the workload's sequences."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    order = np.argsort(w.seq_lens, kind="stable")
+    # Stratified over the sorted lengths: every 8th sequence, starting in the middle of
+    # each group of 8, visited from the middle of the length range outwards.
+    picks = [int(order[i]) for i in range(4, len(order), 8)]
+    picks.sort(key=lambda b: abs(int(np.where(order == b)[0][0]) - len(order) // 2))
+    done, tokens, t_used = [], 0, 0.0
+    errs = []
+    for b in picks:
+        t0 = time.perf_counter()
+        o_ref, lse_ref = oracle.decode_reference(w, batch_indices=[b])
+        t_used += time.perf_counter() - t0
+        done.append(b)
+        tokens += int(w.seq_lens[b])
+        diff = o_gpu[b].astype(np.float64) - o_ref[b]
+        errs.append((np.linalg.norm(diff) / np.linalg.norm(o_ref[b]), np.abs(diff).max(),
+                     np.abs(lse_gpu[b] - lse_ref[b]).max()))
+        if t_used >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    kv = tokens * w.spec.kv_bytes_per_token()
+    rate = kv / t_used / 1e9
+    sample = (f"fp64 oracle on {len(done)} of {w.spec.batch} sequences (stratified by length), "
+              f"{tokens} tokens = {kv / 1e9:.3f} GB of cached rows in {t_used:.1f} s")
+    parity = {"sequences": len(done), "worst_rel_l2": float(max(e[0] for e in errs)),
+              "max_abs": float(max(e[1] for e in errs)), "lse_abs": float(max(e[2] for e in errs))}
+    return {"value": rate, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample}, parity
+
+
+def copy_probe(mib: int):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    x = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 copies of {mib} MiB (read {mib} MiB + write {mib} MiB each)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.SPECS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this size (counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the "
+              "D shards are simulated on one device and no cross-GPU path is built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_attention_sequence_amd as dcp
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dcp.lib()
+    spec = W.SPECS[args.workload]
+    log(f"generating {spec.name} inputs on the host")
+    t0 = time.perf_counter()
+    w = W.make(spec)
+    log(f"generated {w.num_blocks} blocks in {time.perf_counter() - t0:.1f} s; uploading")
+    dev = W.to_torch(w, "cuda")
+    torch.cuda.synchronize()
+    kind = dcp.KV_LATENT if spec.kind == "mla" else dcp.KV_SEPARATE
+    desc = dcp.make_desc(kind, dev.q, dev.k_cache, dev.block_table, num_shards=spec.num_shards,
+                         v_dim=spec.v_dim, softmax_scale=spec.softmax_scale,
+                         max_seq_len=int(w.seq_lens.max()))
+    ws = dcp.alloc_workspace(desc, "cuda")
+    out = torch.empty((spec.batch, spec.num_q_heads, spec.v_dim), dtype=torch.float32,
+                      device="cuda")
+    lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
+
+    def step(events=None):
+        dcp.decode_all_shards(desc, dev.q, dev.k_cache, dev.v_cache, dev.kv_scale,
+                              dev.block_table, dev.seq_lens, workspace=ws, out=out, lse_out=lse,
+                              attn_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+    evs = [(dcp.HipEvent(), dcp.HipEvent()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    attn_ms = float(np.mean([b.elapsed_ms(e) for b, e in evs]))
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, attention kernel {attn_ms:.3f} ms")
+
+    kv_bytes = w.kv_bytes()
+    gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = traffic_from_counters(spec.name)
+    result = {
+        "metric": "decode-attn KV HBM GB/s (% of peak) + tok/s per layer, MLA batch 64, D=8",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.kv_dtype,
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tok_per_s_per_layer": round(spec.batch / (ms_per_step * 1e-3), 1),
+        "config": {
+            "workload": spec.name,
+            "batch": spec.batch,
+            "num_q_heads": spec.num_q_heads,
+            "num_kv_heads": spec.num_kv_heads,
+            "qk_dim": spec.qk_dim,
+            "v_dim": spec.v_dim,
+            "block_size": spec.block_size,
+            "num_shards": spec.num_shards,
+            "sum_seq_len": int(w.seq_lens.sum()),
+            "max_seq_len": int(w.seq_lens.max()),
+            "kv_bytes": kv_bytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_ms": round(attn_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        base, parity = cpu_baseline(w, out.cpu().numpy(), lse.cpu().numpy(), args.cpu_seconds)
+        result["cpu_baseline"] = base
+        result["parity_sample"] = parity
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+// C ABI of libdcp (declared in include/dcp.h): argument validation, workspace
+// carving and the launch sequence plan -> attention -> merge on one stream.
+#include <math.h>
+
+#include "dcp_internal.hpp"
+
+using namespace dcp;
+
+namespace {
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elt_bytes(dcp_dtype_t t) { return t == DCP_F32 ? 4 : (t == DCP_BF16 ? 2 : 1); }
+
+bool valid_dtype(int t) { return t == DCP_F32 || t == DCP_BF16 || t == DCP_FP8_E4M3; }
+
+// Shape and type checks shared by every attention entry point.
+dcp_status_t check_desc(const dcp_attn_desc_t* d) {
+  if (!d || d->struct_size < sizeof(dcp_attn_desc_t)) return DCP_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->qk_dim < 1 ||
+      d->v_dim < 1 || d->block_size < 1 || d->max_blocks_per_seq < 1 || d->num_shards < 1 ||
+      d->max_seq_len < 0 || d->num_cache_blocks < 0)
+    return DCP_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return DCP_ERR_INVALID_ARG;
+  if (!valid_dtype(d->q_dtype) || !valid_dtype(d->kv_dtype) || !valid_dtype(d->out_dtype))
+    return DCP_ERR_INVALID_ARG;
+  if (d->kv_kind != DCP_KV_SEPARATE && d->kv_kind != DCP_KV_LATENT) return DCP_ERR_INVALID_ARG;
+  if (d->kv_kind == DCP_KV_LATENT && (d->num_kv_heads != 1 || d->v_dim > d->qk_dim))
+    return DCP_ERR_INVALID_ARG;
+  if (!isfinite(d->softmax_scale)) return DCP_ERR_INVALID_ARG;
+  const long long cap = static_cast<long long>(d->max_blocks_per_seq) * d->block_size;
+  if (d->max_seq_len > cap) return DCP_ERR_INVALID_ARG;
+  if (static_cast<long long>(d->batch) * d->max_blocks_per_seq >= (1ll << 31) ||
+      static_cast<long long>(d->batch) * d->num_shards >= (1ll << 24) || cap >= (1ll << 31))
+    return DCP_ERR_INVALID_ARG;
+  const int e = elt_bytes(d->kv_dtype);
+  if (d->kv_token_stride <= 0 || d->kv_block_stride <= 0 || d->kv_head_stride < 0)
+    return DCP_ERR_INVALID_ARG;
+  if ((d->kv_token_stride * e) % 16 || (d->kv_block_stride * e) % 16 ||
+      (d->kv_head_stride * e) % 16)
+    return DCP_ERR_INVALID_ARG;
+  if (d->out_dtype == DCP_FP8_E4M3) return DCP_ERR_UNSUPPORTED;
+  if (d->kv_kind == DCP_KV_LATENT ? !mla_supported(d) : !gqa_supported(d))
+    return DCP_ERR_UNSUPPORTED;
+  return DCP_OK;
+}
+
+int groups_for(const dcp_attn_desc_t* d) {
+  return d->kv_kind == DCP_KV_LATENT ? mla_groups() : gqa_groups(d);
+}
+
+dcp_status_t check_tensors(const dcp_attn_desc_t* d, const void* q, const void* k,
+                           const void* v, const float* scale) {
+  if (!q) return DCP_ERR_INVALID_ARG;
+  // An empty cache pool may come with null cache pointers; it is never read.
+  const bool pool = d->num_cache_blocks > 0;
+  if (pool && !k) return DCP_ERR_INVALID_ARG;
+  if (pool && d->kv_kind == DCP_KV_SEPARATE && !v) return DCP_ERR_INVALID_ARG;
+  if (pool && d->kv_dtype == DCP_FP8_E4M3 && !scale) return DCP_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || (k && !aligned(k, 16)) || (v && !aligned(v, 16))) return DCP_ERR_INVALID_ARG;
+  if (scale && !aligned(scale, 4)) return DCP_ERR_INVALID_ARG;
+  return DCP_OK;
+}
+
+dcp_status_t run_attention(const dcp_attn_desc_t* d, const void* q, const void* k, const void* v,
+                           const float* kv_scale, const SegMap& map, int S, void* out,
+                           dcp_dtype_t out_dtype, float* lse_out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream,
+                           hipEvent_t attn_begin = nullptr, hipEvent_t attn_end = nullptr) {
+  const int G = groups_for(d);
+  const size_t need = workspace_bytes_for(S, G, d->num_q_heads, d->v_dim);
+  SegMap m = map;
+  // No cache blocks: every block id is unusable, so every sequence is empty.
+  if (d->num_cache_blocks == 0) m.width = 0;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
+  WorkspaceView ws = carve_workspace(workspace, S, G, d->num_q_heads, d->v_dim);
+  if (launch_plan(m, S, G, ws, stream) != hipSuccess) return DCP_ERR_HIP;
+  AttnLaunch L{d, q, k, v, kv_scale, m, S, ws};
+  if (attn_begin && hipEventRecord(attn_begin, stream) != hipSuccess) return DCP_ERR_HIP;
+  hipError_t err = d->kv_kind == DCP_KV_LATENT ? launch_mla(L, stream) : launch_gqa(L, stream);
+  if (err != hipSuccess) return DCP_ERR_HIP;
+  if (attn_end && hipEventRecord(attn_end, stream) != hipSuccess) return DCP_ERR_HIP;
+  if (launch_merge_pieces(m, ws, G, d->num_q_heads, d->v_dim, out, out_dtype, lse_out, stream) !=
+      hipSuccess)
+    return DCP_ERR_HIP;
+  return DCP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dcp_status_str(dcp_status_t s) {
+  switch (s) {
+    case DCP_OK: return "ok";
+    case DCP_ERR_INVALID_ARG: return "invalid argument";
+    case DCP_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
+    case DCP_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case DCP_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t dcp_version(void) { return kVersion; }
+
+size_t dcp_workspace_size(const dcp_attn_desc_t* d) {
+  if (check_desc(d) != DCP_OK) return 0;
+  const int G = groups_for(d);
+  const int S_all = d->batch * d->num_shards;
+  const size_t a = workspace_bytes_for(S_all, G, d->num_q_heads, d->v_dim);
+  const size_t b = workspace_bytes_for(d->batch, G, d->num_q_heads, d->v_dim);
+  return a > b ? a : b;
+}
+
+dcp_status_t dcp_block_remap(const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                             int32_t max_blocks, int32_t block_size, int32_t num_shards,
+                             int32_t* local_block_table, int32_t* local_seq_lens,
+                             hipStream_t stream) {
+  if (!block_table || !seq_lens || !local_block_table || !local_seq_lens) return DCP_ERR_INVALID_ARG;
+  if (batch < 1 || max_blocks < 1 || block_size < 1 || num_shards < 1) return DCP_ERR_INVALID_ARG;
+  const long long width = (max_blocks + num_shards - 1) / num_shards;
+  if (static_cast<long long>(batch) * max_blocks >= (1ll << 31) ||
+      width * batch * num_shards >= (1ll << 31) ||
+      static_cast<long long>(max_blocks) * block_size >= (1ll << 31))
+    return DCP_ERR_INVALID_ARG;
+  if (launch_remap(block_table, seq_lens, batch, max_blocks, block_size, num_shards,
+                   local_block_table, local_seq_lens, stream) != hipSuccess)
+    return DCP_ERR_HIP;
+  return DCP_OK;
+}
+
+dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* d, const void* q, const void* k_cache,
+                                const void* v_cache, const float* kv_scale,
+                                const int32_t* local_block_table, const int32_t* local_seq_lens,
+                                float* o_partial, float* lse_partial, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  dcp_status_t st = check_desc(d);
+  if (st != DCP_OK) return st;
+  if ((st = check_tensors(d, q, k_cache, v_cache, kv_scale)) != DCP_OK) return st;
+  if (!local_block_table || !local_seq_lens || !o_partial || !lse_partial)
+    return DCP_ERR_INVALID_ARG;
+  if (!aligned(o_partial, 16)) return DCP_ERR_INVALID_ARG;
+  if (d->batch == 0) return DCP_OK;
+  SegMap map;
+  map.table = local_block_table;
+  map.lens = local_seq_lens;
+  map.width = (d->max_blocks_per_seq + d->num_shards - 1) / d->num_shards;
+  map.D = 1;
+  map.bs = d->block_size;
+  map.batch = d->batch;
+  return run_attention(d, q, k_cache, v_cache, kv_scale, map, d->batch, o_partial, DCP_F32,
+                       lse_partial, workspace, workspace_bytes, stream);
+}
+
+dcp_status_t dcp_lse_merge(const float* o_partials, const float* lse_partials,
+                           int32_t num_partials, int32_t batch, int32_t num_heads, int32_t v_dim,
+                           void* out, dcp_dtype_t out_dtype, float* lse_out, hipStream_t stream) {
+  if (!o_partials || !lse_partials || !out) return DCP_ERR_INVALID_ARG;
+  if (num_partials < 1 || batch < 1 || num_heads < 1 || v_dim < 4) return DCP_ERR_INVALID_ARG;
+  if (out_dtype != DCP_F32 && out_dtype != DCP_BF16) return DCP_ERR_INVALID_ARG;
+  if (static_cast<long long>(num_partials) * batch * num_heads * v_dim >= (1ll << 40))
+    return DCP_ERR_INVALID_ARG;
+  if (v_dim % 4 || v_dim > 1024) return DCP_ERR_UNSUPPORTED;
+  if (!aligned(o_partials, 16) || !aligned(out, out_dtype == DCP_F32 ? 16 : 8))
+    return DCP_ERR_INVALID_ARG;
+  if (launch_merge_partials(o_partials, lse_partials, num_partials, batch, num_heads, v_dim, out,
+                            out_dtype, lse_out, stream) != hipSuccess)
+    return DCP_ERR_HIP;
+  return DCP_OK;
+}
+
+dcp_status_t dcp_decode_all_shards(const dcp_attn_desc_t* d, const void* q, const void* k_cache,
+                                   const void* v_cache, const float* kv_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens, void* out,
+                                   float* lse_out, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  return dcp_decode_all_shards_timed(d, q, k_cache, v_cache, kv_scale, block_table, seq_lens, out,
+                                     lse_out, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+dcp_status_t dcp_decode_all_shards_timed(const dcp_attn_desc_t* d, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const float* kv_scale, const int32_t* block_table,
+                                         const int32_t* seq_lens, void* out, float* lse_out,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream, hipEvent_t attn_begin,
+                                         hipEvent_t attn_end) {
+  dcp_status_t st = check_desc(d);
+  if (st != DCP_OK) return st;
+  if ((st = check_tensors(d, q, k_cache, v_cache, kv_scale)) != DCP_OK) return st;
+  if (!block_table || !seq_lens || !out) return DCP_ERR_INVALID_ARG;
+  if (!aligned(out, d->out_dtype == DCP_F32 ? 16 : 8)) return DCP_ERR_INVALID_ARG;
+  if (d->batch == 0) return DCP_OK;
+  SegMap map;
+  map.table = block_table;
+  map.lens = seq_lens;
+  map.width = d->max_blocks_per_seq;
+  map.D = d->num_shards;
+  map.bs = d->block_size;
+  map.batch = d->batch;
+  return run_attention(d, q, k_cache, v_cache, kv_scale, map, d->batch * d->num_shards, out,
+                       d->out_dtype, lse_out, workspace, workspace_bytes, stream, attn_begin,
+                       attn_end);
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+// Internal declarations shared by the libdcp translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dcp.h"
+
+namespace dcp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+#define DCP_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Work plan.
+//
+// The tokens of one decode call are organised in segments: segment s is the
+// pair (sequence b = s / D, shard r = s % D) and holds the cache blocks of
+// sequence b that shard r owns, in local order i = 0, 1, ...; local block i
+// is column r + D * i of row b of the block table. With D = 1 and r = 0 the
+// same description covers one shard's local table.
+//
+// A planning kernel counts the blocks of every segment and writes their
+// prefix sums. The attention kernels then split the concatenation of all
+// segments into G equal ranges of `chunk` blocks, one per work group, so every
+// work group streams the same number of cache blocks whatever the length mix.
+// Where a range crosses a segment boundary the work group emits one partial
+// (O, LSE) per segment piece; the piece of segment s handled by work group g
+// is stored in slot s + g, which is unique because both s and g grow along
+// the concatenation. Slots used <= S + G - 1.
+// ---------------------------------------------------------------------------
+struct PlanHeader {
+  int32_t chunk;  // blocks per work group (>= 1)
+  int32_t total;  // blocks over all segments
+};
+// Workspace layout: PlanHeader, seg_off[S + 1] (int32), then at 256-byte
+// alignment lse slots [num_slots, Hq] fp32, then o slots [num_slots, Hq, v_dim] fp32.
+
+struct SegMap {
+  const int32_t* table;  // [B, width]
+  const int32_t* lens;   // [B], tokens (global, or this shard's local count)
+  int32_t width;         // table row width
+  int32_t D;             // segments per sequence
+  int32_t bs;            // block size
+  int32_t batch;
+};
+
+// Tokens of sequence b, clamped to what its table row can address.
+__device__ __forceinline__ int seq_tokens(const SegMap& m, int b) {
+  int L = m.lens[b];
+  int cap = m.width * m.bs;
+  L = L < 0 ? 0 : L;
+  return L > cap ? cap : L;
+}
+
+__device__ __forceinline__ int segment_blocks(const SegMap& m, int s) {
+  int b = s / m.D, r = s - b * m.D;
+  int L = seq_tokens(m, b);
+  int nb = (L + m.bs - 1) / m.bs;
+  return nb > r ? (nb - r + m.D - 1) / m.D : 0;
+}
+
+// Token range of one piece: local blocks [i0, i1) of segment s.
+struct Piece {
+  int s, b, r;
+  int i0, i1;
+  int L;     // tokens of the whole sequence (clamped)
+  int ntok;  // tokens covered by this piece
+};
+
+__device__ __forceinline__ Piece make_piece(const SegMap& m, int s, int i0, int i1) {
+  Piece p;
+  p.s = s;
+  p.b = s / m.D;
+  p.r = s - p.b * m.D;
+  p.i0 = i0;
+  p.i1 = i1;
+  p.L = seq_tokens(m, p.b);
+  int last_col = p.r + m.D * (i1 - 1);
+  int full = (i1 - i0) * m.bs;
+  int tail = m.bs * (last_col + 1) - p.L;  // > 0 only for the sequence's last block
+  p.ntok = full - (tail > 0 ? tail : 0);
+  return p;
+}
+
+// Table column of the local block holding piece token tau.
+__device__ __forceinline__ int piece_col(const SegMap& m, const Piece& p, int tau) {
+  return p.r + m.D * (p.i0 + tau / m.bs);
+}
+
+// Segment containing concatenated block index x (seg_off non-decreasing,
+// seg_off[0] = 0, x < seg_off[S]).
+__device__ __forceinline__ int find_segment(const int32_t* seg_off, int S, int x) {
+  int lo = 0, hi = S;  // answer in [0, S)
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (seg_off[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Logical work-group index with consecutive ranges kept on one XCD: hardware
+// dispatches work group i to XCD i % 8, so groups that share a sequence (and
+// its query rows) read them through the same L2.
+__device__ __forceinline__ int xcd_logical_group(int i, int G) {
+  int per = G >> 3;
+  return (i & 7) * per + (i >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// Small device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (defined in the .hip files)
+// ---------------------------------------------------------------------------
+struct WorkspaceView {
+  PlanHeader* header;
+  int32_t* seg_off;
+  float* lse;
+  float* o;
+  int num_slots;
+};
+
+size_t workspace_bytes_for(int S, int G, int Hq, int v_dim);
+WorkspaceView carve_workspace(void* ws, int S, int G, int Hq, int v_dim);
+
+hipError_t launch_plan(const SegMap& m, int S, int G, WorkspaceView ws, hipStream_t stream);
+hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, int G, int Hq, int v_dim,
+                               void* out, dcp_dtype_t out_dtype, float* lse_out,
+                               hipStream_t stream);
+hipError_t launch_merge_partials(const float* o, const float* lse, int P, int B, int H, int v_dim,
+                                 void* out, dcp_dtype_t out_dtype, float* lse_out,
+                                 hipStream_t stream);
+hipError_t launch_remap(const int32_t* table, const int32_t* lens, int B, int max_blocks, int bs,
+                        int D, int32_t* local_table, int32_t* local_lens, hipStream_t stream);
+
+struct AttnLaunch {
+  const dcp_attn_desc_t* desc;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* kv_scale;
+  SegMap map;
+  int S;
+  WorkspaceView ws;
+};
+
+// Work groups per launch for each kernel family (a property of the kernel, not
+// of the device, so workspace sizes are pure functions of the descriptor).
+int mla_groups();
+int gqa_groups(const dcp_attn_desc_t* desc);
+bool mla_supported(const dcp_attn_desc_t* desc);
+bool gqa_supported(const dcp_attn_desc_t* desc);
+hipError_t launch_mla(const AttnLaunch& a, hipStream_t stream);
+hipError_t launch_gqa(const AttnLaunch& a, hipStream_t stream);
+
+}  // namespace dcp

@@ -1,0 +1,194 @@
+/*
+ * dcp.h -- C ABI of libdcp: sharded paged decode attention for AMD MI355X (gfx950).
+ *
+ * Decode Context Parallelism shards a sequence's paged KV cache along the
+ * sequence: logical block j of a sequence belongs to shard j % D
+ * ("vLLM长序列推理优化：DCP切分KV Cache原理与实战", section 2.2). Each shard
+ * attends the full single-token query against its own blocks and produces a
+ * partial output O_i with its log-sum-exp LSE_i; the partials are combined as
+ *     O = sum_i exp(LSE_i) / sum_j exp(LSE_j) * O_i
+ * ("Efficient Decode Context Parallelism with vLLM for Long Context
+ * Workloads", summary section, merge equation, and section A2). On one GPU the
+ * D shards are D interleaved block subsets of one cache.
+ *
+ * Conventions for every entry point
+ *  - Pointers named *_table, *_lens, q, k_cache, v_cache, kv_scale, out,
+ *    o_*, lse_* and workspace are DEVICE pointers; descriptors and scalars are
+ *    host values. The caller owns and allocates every buffer; the library
+ *    never allocates, frees or keeps pointers after the enqueued work ends.
+ *  - Every call only enqueues work on `stream` (0 = the default stream) and
+ *    returns without synchronising, so calls can be captured in a HIP graph.
+ *    The library keeps no mutable global state and is thread-safe.
+ *  - Host-visible arguments are validated before anything is enqueued; on an
+ *    error nothing is enqueued and the call returns a non-zero status.
+ *    DCP_ERR_HIP reports a launch error from the HIP runtime.
+ *  - Device-resident integers (block tables, lengths) are not validated.
+ *    Lengths are clamped to the table width times the block size; a table
+ *    entry outside [0, num_cache_blocks) is skipped (its tokens contribute
+ *    nothing), so no out-of-range cache address is ever formed. A pool of
+ *    num_cache_blocks = 0 is allowed (cache pointers may then be NULL) and
+ *    makes every sequence empty.
+ *  - seq_len counts every cached token of the sequence, including the one just
+ *    written; decode attends to all of them with no mask, since keys are
+ *    cached after the rotary embedding ("vLLM长序列推理优化", section 3.4).
+ *  - An empty token set (seq_len 0, or a shard that owns no block) yields
+ *    O = 0 and LSE = -inf; such a partial has weight 0 in every merge.
+ *  - LSE values are natural logarithms of sum_t exp(softmax_scale * q.k_t).
+ *  - All layouts are row-major with the last dimension contiguous.
+ */
+#ifndef DCP_H_
+#define DCP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DCP_OK = 0,
+  DCP_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad stride or alignment */
+  DCP_ERR_UNSUPPORTED = 2, /* a valid combination this build has no kernel for */
+  DCP_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dcp_workspace_size() */
+  DCP_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} dcp_status_t;
+
+typedef enum { DCP_F32 = 0, DCP_BF16 = 1, DCP_FP8_E4M3 = 2 } dcp_dtype_t;
+
+typedef enum {
+  /* Grouped-query attention: separate K and V caches [num_cache_blocks,
+   * block_size, num_kv_heads, dim]; query head h reads KV head
+   * h / (num_q_heads / num_kv_heads) ("tensor broadcast" of the shared head). */
+  DCP_KV_SEPARATE = 0,
+  /* Absorbed multi-head latent attention: one latent row of qk_dim values per
+   * token [num_cache_blocks, block_size, qk_dim], shared by every query head;
+   * scores use all qk_dim columns and the value is the first v_dim columns. */
+  DCP_KV_LATENT = 1
+} dcp_kv_kind_t;
+
+/* Shape and types of one decode-attention layer call. */
+typedef struct {
+  uint32_t struct_size;      /* sizeof(dcp_attn_desc_t), for ABI versioning */
+  int32_t batch;             /* B, sequences (one query token each) */
+  int32_t num_q_heads;       /* Hq */
+  int32_t num_kv_heads;      /* Hkv; must be 1 for DCP_KV_LATENT */
+  int32_t qk_dim;            /* width of q and k (the latent width for MLA) */
+  int32_t v_dim;             /* width of v and of the output */
+  int32_t block_size;        /* tokens per cache block */
+  int32_t max_blocks_per_seq;/* width of the global block table */
+  int32_t num_shards;        /* D >= 1 */
+  int32_t max_seq_len;       /* host upper bound of any seq_len (sizes the workspace) */
+  int32_t num_cache_blocks;  /* physical blocks in the cache pool (>= 0) */
+  dcp_kv_kind_t kv_kind;
+  dcp_dtype_t q_dtype;       /* DCP_F32 or DCP_BF16 */
+  dcp_dtype_t kv_dtype;      /* DCP_F32, DCP_BF16 or DCP_FP8_E4M3 (latent only) */
+  dcp_dtype_t out_dtype;     /* final output of dcp_decode_all_shards: DCP_F32 or DCP_BF16 */
+  float softmax_scale;       /* score = softmax_scale * q . k */
+  int64_t kv_block_stride;   /* elements between cache blocks */
+  int64_t kv_token_stride;   /* elements between tokens of a block */
+  int64_t kv_head_stride;    /* elements between KV heads of a token (0 for latent) */
+} dcp_attn_desc_t;
+
+/* Supported kernels in this build:
+ *   DCP_KV_SEPARATE: q_dtype == kv_dtype in {F32, BF16}; qk_dim == v_dim in
+ *     {64, 128}; num_q_heads % num_kv_heads == 0.
+ *   DCP_KV_LATENT: q BF16; kv BF16, or FP8_E4M3 with kv_scale; qk_dim 576,
+ *     v_dim 512; num_q_heads 16, 32 or a multiple of 64 up to 256. With an
+ *     FP8 cache the products run in fp16: query values must lie inside the
+ *     fp16 range (|q| <= 65504) and scales must not exceed 65504.
+ * Cache rows (the qk_dim / v_dim values of one token and head) must start on
+ * a 16-byte boundary. */
+
+/* Global block table -> per-shard local tables.
+ * "vLLM长序列推理优化", sections 2.2 and 3.2: shard r keeps the blocks j with
+ * j % D == r, and global block j is local block j / D there.
+ *   block_table       [batch, max_blocks] int32, physical id of logical block j
+ *   seq_lens          [batch] int32
+ *   local_block_table [num_shards, batch, ceil(max_blocks / num_shards)] int32 (out);
+ *                     entry [r, b, i] = block_table[b, r + D*i] for every owned
+ *                     block, -1 elsewhere
+ *   local_seq_lens    [num_shards, batch] int32 (out): tokens shard r holds of
+ *                     sequence b (the last block may be partly filled)
+ * Bit-exact integer work. */
+dcp_status_t dcp_block_remap(const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                             int32_t max_blocks, int32_t block_size, int32_t num_shards,
+                             int32_t* local_block_table, int32_t* local_seq_lens,
+                             hipStream_t stream);
+
+/* Bytes of device workspace dcp_decode_partial and dcp_decode_all_shards need
+ * for this descriptor (the larger of the two), or 0 if the descriptor is
+ * invalid or unsupported. The workspace holds split partials and a small
+ * work plan; it need not be initialised and may be reused between calls that
+ * are ordered on one stream. */
+size_t dcp_workspace_size(const dcp_attn_desc_t* desc);
+
+/* One shard's partial attention (the "Compute" step of section A2 of the
+ * DCP blog summary): attends every query head to the tokens of one shard.
+ *   q                 [batch, num_q_heads, qk_dim] (q_dtype)
+ *   k_cache, v_cache  cache pools as described by desc (v_cache NULL for latent)
+ *   kv_scale          [num_cache_blocks, block_size] fp32 per-token scale for FP8, else NULL
+ *   local_block_table [batch, ceil(max_blocks_per_seq / num_shards)] int32, this
+ *                     shard's rows of dcp_block_remap's output
+ *   local_seq_lens    [batch] int32, this shard's token counts
+ *   o_partial         [batch, num_q_heads, v_dim] fp32 (out), normalised output
+ *   lse_partial       [batch, num_q_heads] fp32 (out)
+ * desc->num_shards only sizes the local table width here. */
+dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
+                                const void* v_cache, const float* kv_scale,
+                                const int32_t* local_block_table, const int32_t* local_seq_lens,
+                                float* o_partial, float* lse_partial, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* LSE merge of num_partials partial results (summary section of the DCP blog
+ * page, merge equation; the reweighting inside cp_lse_ag_out_rs of section A2):
+ *   o_partials   [num_partials, batch, num_heads, v_dim] fp32
+ *   lse_partials [num_partials, batch, num_heads] fp32 (-inf marks an empty partial;
+ *                its o_partials rows are never read)
+ *   out          [batch, num_heads, v_dim] of out_dtype (DCP_F32 or DCP_BF16)
+ *   lse_out      [batch, num_heads] fp32, ln sum_i exp(LSE_i), or NULL */
+dcp_status_t dcp_lse_merge(const float* o_partials, const float* lse_partials,
+                           int32_t num_partials, int32_t batch, int32_t num_heads, int32_t v_dim,
+                           void* out, dcp_dtype_t out_dtype, float* lse_out, hipStream_t stream);
+
+/* All D shards of one layer on one GPU, fused: ownership j % D is applied on
+ * the fly to the global block table, every shard's blocks are attended in
+ * parallel splits, and one LSE merge over all shards and splits produces the
+ * unsharded result (the whole AllGather-Q / Compute / AllGather+ReduceScatter
+ * round of section A2, with the collectives replaced by on-device data).
+ *   block_table [batch, max_blocks_per_seq] int32 (global), seq_lens [batch] int32
+ *   out         [batch, num_q_heads, v_dim] of desc->out_dtype
+ *   lse_out     [batch, num_q_heads] fp32 or NULL
+ * Other arguments as in dcp_decode_partial. */
+dcp_status_t dcp_decode_all_shards(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
+                                   const void* v_cache, const float* kv_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens, void* out,
+                                   float* lse_out, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* dcp_decode_all_shards with timing hooks for profilers and benchmarks: the
+ * same work, plus `attn_begin` / `attn_end` (events created by the caller)
+ * recorded on `stream` immediately before and after the attention kernel,
+ * so hipEventElapsedTime gives that kernel's duration alone. Either event may
+ * be NULL. */
+dcp_status_t dcp_decode_all_shards_timed(const dcp_attn_desc_t* desc, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const float* kv_scale, const int32_t* block_table,
+                                         const int32_t* seq_lens, void* out, float* lse_out,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream, hipEvent_t attn_begin,
+                                         hipEvent_t attn_end);
+
+/* Static text for a status code. */
+const char* dcp_status_str(dcp_status_t status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t dcp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCP_H_ */

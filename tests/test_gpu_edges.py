@@ -1,0 +1,80 @@
+"""Edge cases on the GPU: empty and ragged sequences, tiny and odd block sizes,
+shard counts above the block count, other head counts, and unusable block ids."""
+import numpy as np
+import pytest
+
+import decode_attention_sequence_amd as dcp
+import oracle
+import workloads as W
+from gpu_helpers import TOL, compare, need_gpu, run_all_shards, run_per_shard
+
+pytestmark = pytest.mark.gpu
+
+EDGE_LENS = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 129, 1000]
+
+CASES = [
+    # kind, kv dtype, block size, shards, Hq, Hkv, qk_dim
+    ("mla", "bf16", 64, 8, 64, 1, 576),
+    ("mla", "fp8", 64, 8, 64, 1, 576),
+    ("mla", "bf16", 16, 4, 64, 1, 576),
+    ("mla", "fp8", 32, 3, 32, 1, 576),
+    ("mla", "bf16", 128, 2, 128, 1, 576),
+    ("mla", "bf16", 1, 8, 16, 1, 576),
+    ("mla", "fp8", 48, 5, 64, 1, 576),
+    ("gqa", "bf16", 16, 4, 64, 8, 128),
+    ("gqa", "bf16", 16, 3, 16, 1, 64),
+    ("gqa", "bf16", 8, 2, 32, 2, 128),
+    ("gqa", "bf16", 5, 7, 12, 4, 64),
+    ("gqa", "f32", 16, 2, 4, 1, 64),
+    ("gqa", "f32", 5, 3, 8, 2, 128),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _workload(kind, dtype, bs, d, hq, hkv, dim, lens, seed=11):
+    return W.custom(kind, lens, num_q_heads=hq, num_kv_heads=hkv, qk_dim=dim,
+                    v_dim=512 if kind == "mla" else dim, block_size=bs, num_shards=d,
+                    kv_dtype=dtype, seed=seed)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_edge_lengths(case):
+    w = _workload(*case, EDGE_LENS)
+    o_ref, lse_ref = oracle.decode_reference(w)
+    o, lse, dev, _ = run_all_shards(w)
+    compare(o, lse, o_ref, lse_ref, **TOL[case[1]], label="all shards")
+    op, lp, _, _ = run_per_shard(w, dev)
+    opr, lpr = oracle.shard_partials(w)
+    for r in range(case[3]):
+        compare(op[r], lp[r], opr[r], lpr[r], **TOL[case[1]], label=f"shard {r}")
+
+
+def test_all_sequences_empty():
+    w = _workload("mla", "bf16", 64, 8, 64, 1, 576, [0, 0, 0])
+    o, lse, _, _ = run_all_shards(w)
+    assert float(o.abs().max()) == 0.0 and bool((lse == -np.inf).all())
+
+
+@pytest.mark.parametrize("kind,dtype", [("mla", "bf16"), ("mla", "fp8"), ("gqa", "bf16"),
+                                        ("gqa", "f32")])
+def test_unusable_block_ids_are_skipped(kind, dtype):
+    dim = 576 if kind == "mla" else 128
+    bs = 64 if kind == "mla" else 16
+    w = _workload(kind, dtype, bs, 4, 64 if kind == "mla" else 16, 1 if kind == "mla" else 2,
+                  dim, [5 * bs + 7, 3 * bs, 2 * bs + 1])
+    bad = {0: [1, 4], 1: [2], 2: [0]}
+    for b, blocks in bad.items():
+        for j in blocks:
+            w.block_table[b, j] = -7 if j % 2 else w.num_blocks + 3
+    o_ref = np.zeros((3, w.spec.num_q_heads, w.spec.v_dim))
+    lse_ref = np.zeros((3, w.spec.num_q_heads))
+    for b in range(3):
+        pos = [t for t in range(int(w.seq_lens[b])) if t // bs not in bad[b]]
+        k, v = oracle.sequence_kv(w, b, np.array(pos))
+        o_ref[b], lse_ref[b] = oracle.attend(oracle.query(w, b), k, v, w.spec.softmax_scale)
+    o, lse, _, _ = run_all_shards(w)
+    compare(o, lse, o_ref, lse_ref, **TOL[dtype], label="skipped ids")

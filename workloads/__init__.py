@@ -288,3 +288,29 @@ def custom(kind: str, seq_lens, *, num_q_heads: int, num_kv_heads: int = 1, qk_d
                 num_shards, kv_dtype, "explicit",
                 softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(qk_dim), seed)
     return _build(spec, lens)
+
+
+def to_torch(w: Workload, device="cuda"):
+    """Device tensors of a workload (plain copies; bf16 bit patterns become torch.bfloat16,
+    e4m3 codes stay uint8). Returns a namespace with q, k_cache, v_cache, kv_scale,
+    block_table and seq_lens."""
+    import torch
+    from types import SimpleNamespace
+
+    def dev(x, bf16=False):
+        if x is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        if bf16:
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(device)
+
+    bf = w.spec.kv_dtype == "bf16"
+    return SimpleNamespace(
+        q=dev(w.q, w.spec.q_dtype == "bf16"),
+        k_cache=dev(w.k_cache, bf),
+        v_cache=dev(w.v_cache, bf),
+        kv_scale=dev(w.kv_scale),
+        block_table=dev(w.block_table),
+        seq_lens=dev(w.seq_lens),
+    )

@@ -9,25 +9,31 @@
 // lives in latent space (qk_dim = 576 = 512 latent + 64 rotary columns): the
 // score is q . c over all 576 columns and the value is c[0:512].
 //
-// Kernel design (one work group per CU, one stream-K range of cache blocks
-// per work group, up to 64 query heads per work group):
-//  * wave w owns query heads 16w .. 16w+15 and keeps their query rows in
-//    registers as MFMA B fragments for the whole range;
+// Kernel design: one work group per CU processes one stream-K range of cache
+// blocks for up to 64 query heads, split into HG groups of 16 heads, with
+// 2 * HG waves (two per SIMD at 64 heads):
 //  * 32-token latent tiles (36 KB bf16) are copied HBM -> LDS with 16-byte
-//    direct-to-LDS loads through a 4-stage ring, so three tiles (108 KB) are
-//    in flight per CU while one is consumed; each wave issues a fixed number
-//    of copies per tile, so `s_waitcnt vmcnt(n)` names exactly the tiles
-//    still in flight. Rows past the end of the range (or with an unusable
-//    block id) are copied from a safe address and zero-filled once landed;
-//  * S^T[t][h] = C_tile . Q^T with v_mfma_f32_16x16x32_bf16 (A = latent rows
-//    from LDS, B = query fragments), so each lane ends up holding one head's
-//    scores for 8 tokens -- exactly the B-operand layout of the next product;
-//  * online softmax per head in the exp2 domain; the running reference max is
-//    only raised (and the accumulator rescaled) when a tile's max exceeds it
-//    by more than 8, so probabilities stay <= 256 and rescales are rare;
-//  * O^T[v][h] += C_tile^T . P^T with the same MFMA, the transposed A operand
-//    read from the same LDS tile by ds_read_b64_tr_b16, so every latent byte
-//    is fetched from HBM once and serves both products;
+//    direct-to-LDS loads through a 4-stage ring, three tiles in flight; every
+//    wave issues a fixed number of copies per tile, so `s_waitcnt vmcnt(n)`
+//    names exactly the tiles still in flight. Rows past the end of the range
+//    (or with an unusable block id) are read from a safe in-pool address and
+//    zero-filled once landed;
+//  * scores: wave (g, t) computes S^T for the 16 tokens of half t of the tile
+//    and the 16 heads of group g, S^T = C_tile . Q^T with
+//    v_mfma_f32_16x16x32_bf16 (A = latent rows from LDS, B = the heads' query
+//    rows held in registers for the whole range);
+//  * online softmax in the exp2 domain: the two token halves exchange their
+//    per-head maxima through LDS, so every wave tracks the same reference max
+//    for every head; the reference only rises (and accumulators are
+//    rescaled) when a tile's max exceeds it by more than 8, so rescales are
+//    rare and probabilities stay <= 256;
+//  * values: probabilities go through LDS once (8 bytes per lane) and wave w
+//    computes O^T for its 512 / (2 HG)-column slice of the value dimension for
+//    all heads, O^T += C_tile^T . P^T, the transposed A operand read from the
+//    same LDS tile by ds_read_b64_tr_b16 -- every latent byte is fetched from
+//    HBM once and serves both products, and each transposed byte is read once;
+//  * LDS fragment reads are issued ahead of their MFMAs through register rings
+//    (inline asm with explicit lgkmcnt waits tied to the destination registers);
 //  * the fp8 variant copies e4m3 codes and one fp32 scale per token, widens
 //    the codes to fp16 in LDS (exact) one tile ahead of the MFMAs and runs
 //    both products as v_mfma_f32_16x16x32_f16 (query converted bf16 -> fp16);
@@ -41,37 +47,31 @@ namespace {
 
 constexpr int kQK = 576;
 constexpr int kV = 512;
-constexpr int kHeadsPerGroup = 64;         // query heads per work group
 constexpr int kT = 32;                     // tokens per tile
-constexpr int kRowB = kQK * 2;             // bf16 row bytes (1152)
+constexpr int kRowB = kQK * 2;             // 16-bit row bytes (1152)
 constexpr int kRowCh = kRowB / 16;         // 16-byte chunks per row (72)
 constexpr int kTileB = kT * kRowB;         // 36864
 constexpr int kTileCh = kT * kRowCh;       // 2304
 constexpr int kDmaInst = kTileCh / 64;     // 36 wave-wide copies per bf16 tile
 constexpr int kKSteps = kQK / 32;          // 18
-constexpr int kVTiles = kV / 16;           // 32
 constexpr int kF8RowB = kQK;               // 576 code bytes per row
 constexpr int kF8TileB = kT * kF8RowB;     // 18432
 constexpr int kF8RowCh = kF8RowB / 16;     // 36
 constexpr int kF8DmaInst = kF8TileB / 1024;  // 18
 constexpr int kGroups = 256;               // work groups per head group (one per CU)
 constexpr int kStages = 4;                 // copy ring depth
-constexpr int kIdWin = 2048;               // block ids staged in LDS at a time
+constexpr int kIdWin = 512;                // block ids staged in LDS at a time
 constexpr int kPadB = 1024;                // landing pad for filler copies
-constexpr int kScaleB = 256;               // per-wave scale landing area per stage
-
-// LDS layouts.
-//   bf16: [kStages tiles][ids][pad]
-//   fp8 : [kStages code tiles][2 bf16 tiles][scales: kStages x NW x 256 B][ids][pad]
-constexpr int kLdsBf16 = kStages * kTileB + kIdWin * 4 + kPadB;
-template <int NW>
-constexpr int lds_fp8() { return kStages * kF8TileB + 2 * kTileB + kStages * NW * kScaleB + kIdWin * 4 + kPadB; }
+constexpr int kSDist = 4;                  // S^T: K steps of A fragments read ahead
+constexpr int kSRing = kSDist + 2;         // ring slot reused two MFMA steps after its use
 
 // Row swizzle: logical chunk c of row r sits at (c & ~7) | ((c & 7) ^ swz(r)).
-// With 1152-byte rows this keeps both access patterns below free of LDS bank
-// conflicts: 16 rows x one 16-byte chunk (MFMA A fragments) and 4 rows x 32
-// bytes per 16-lane group (transposed reads).
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// With 1152-byte rows the two read patterns are 16 rows x one 16-byte chunk
+// (MFMA A fragments, ds_read_b128) and 4 rows x 32 bytes per 16-lane group
+// (ds_read_b64_tr_b16). Among the XOR swizzles measured on MI355X this one
+// gives both patterns their full LDS rate (about 200 B/clk per CU for the
+// 16-byte reads, 125 B/clk for the transposed reads; unswizzled rows reach 61).
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ (r & 1); }
 __device__ __forceinline__ int chunk_off(int r, int c) {
   return r * kRowB + 16 * ((c & ~7) | ((c & 7) ^ swz(r)));
 }
@@ -93,14 +93,42 @@ struct MlaArgs {
   float scale_log2;
 };
 
-__device__ __forceinline__ bf16x8 lds_read_b128(const DCP_LDS char* p) {
-  return *reinterpret_cast<const DCP_LDS bf16x8*>(p);
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
-__device__ __forceinline__ s16x4 lds_read_tr(const DCP_LDS char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<DCP_LDS s16x4*>(const_cast<DCP_LDS char*>(p)));
+// LDS fragment reads as inline asm: the compiler does not treat them as reads
+// that may alias the in-flight direct-to-LDS copies (it would otherwise wait
+// for every copy before each one), and the explicit waits below order them.
+template <int OFF>
+__device__ __forceinline__ void lds_b128(i32x4& r, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
 }
+template <int OFF>
+__device__ __forceinline__ void lds_tr(i32x2& r, uint32_t addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+}
+// Wait until at most N LDS operations are outstanding; the operand ties the
+// awaited registers so their consumers cannot move above the wait.
+template <int N, class T0>
+__device__ __forceinline__ void wait_lgkm(T0& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+template <int N, class T0, class T1>
+__device__ __forceinline__ void wait_lgkm(T0& a, T1& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+
+// A value every lane holds identically, moved to a scalar register.
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
@@ -108,6 +136,10 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // e4m3 codes -> fp16, exact: every e4m3 value (4 significant bits, |x| <= 448,
 // down to 2^-9) is an fp16 normal or subnormal number.
@@ -117,8 +149,6 @@ __device__ __forceinline__ uint32_t f8x2_to_f16x2(uint32_t codes) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[1]));
 }
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
 // MFMA element type: bf16 for a bf16 cache; fp16 for an fp8 cache, whose codes
 // widen to fp16 exactly and whose probability-times-scale products then keep
 // 11 significant bits instead of 8.
@@ -127,20 +157,23 @@ struct Elt;
 template <>
 struct Elt<false> {
   typedef bf16x8 vec;
-  static __device__ __forceinline__ f32x4 mfma(vec a, vec b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  static __device__ __forceinline__ f32x4 mfma(i32x4 a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(vec, a), b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint16_t from_f32(float x) { return f32_to_bf16_bits(x); }
+  // two fp32 -> packed pair, round to nearest even (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+  }
   static __device__ __forceinline__ vec from_bf16(bf16x8 v) { return v; }
 };
 template <>
 struct Elt<true> {
   typedef f16x8 vec;
-  static __device__ __forceinline__ f32x4 mfma(vec a, vec b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  static __device__ __forceinline__ f32x4 mfma(i32x4 a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(vec, a), b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint16_t from_f32(float x) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, f16x2));
   }
   // bf16 -> fp16 (exact inside the fp16 range).
   static __device__ __forceinline__ vec from_bf16(bf16x8 v) {
@@ -151,26 +184,33 @@ struct Elt<true> {
   }
 };
 
-template <int NW, bool FP8>
-struct MlaCfg {
+// Static configuration: HG groups of 16 heads, 2 * HG waves.
+template <int HG, bool FP8>
+struct Cfg {
+  static constexpr int NW = 2 * HG;
+  static constexpr int kMT = 32 / NW;                          // value M tiles per wave
   static constexpr int kInst = FP8 ? kF8DmaInst : kDmaInst;
-  static constexpr int kPerWave = (kInst + NW - 1) / NW;        // copies per wave per tile
-  static constexpr int kOps = kPerWave + (FP8 ? 1 : 0);          // + the scale copy
-  static constexpr int kLds = FP8 ? lds_fp8<NW>() : kLdsBf16;
+  static constexpr int kPerWave = (kInst + NW - 1) / NW;      // tile copies per wave
+  static constexpr int kOps = kPerWave + (FP8 ? 1 : 0);        // + the scale copy
   static constexpr int kStageB = FP8 ? kF8TileB : kTileB;
-  static constexpr int kIdsOff = FP8 ? kStages * kF8TileB + 2 * kTileB + kStages * NW * kScaleB
-                                     : kStages * kTileB;
+  // LDS layout
+  static constexpr int kRingOff = 0;
+  static constexpr int kF16Off = kStages * kF8TileB;          // fp8: two fp16 tiles
+  static constexpr int kScaleOff = kF16Off + 2 * kTileB;       // fp8: kStages x 256 B
+  static constexpr int kPOff = FP8 ? kScaleOff + kStages * 256 : kStages * kTileB;
+  static constexpr int kMxOff = kPOff + HG * 64 * 16;          // [2][16][4] floats
+  static constexpr int kLsumOff = kMxOff + 2 * 16 * 4 * 4;     // [2][64] floats
+  static constexpr int kIdsOff = kLsumOff + 2 * 64 * 4;
   static constexpr int kPadOff = kIdsOff + kIdWin * 4;
-  static constexpr int kBf16Off = kStages * kF8TileB;            // fp8 only
-  static constexpr int kScaleOff = kStages * kF8TileB + 2 * kTileB;  // fp8 only
+  static constexpr int kLds = kPadOff + kPadB;
+  static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
 // Wait until at most n_after tiles (C::kOps operations each) issued after the
 // awaited one are still in flight. The hardware counter saturates at 63, so
 // larger counts are clamped, which only waits for more.
-template <int NW, bool FP8>
+template <class C>
 __device__ __forceinline__ void wait_tiles_after(int n_after) {
-  using C = MlaCfg<NW, FP8>;
   constexpr int k1 = C::kOps > 63 ? 63 : C::kOps;
   constexpr int k2 = 2 * C::kOps > 63 ? 63 : 2 * C::kOps;
   switch (n_after) {
@@ -180,21 +220,43 @@ __device__ __forceinline__ void wait_tiles_after(int n_after) {
   }
 }
 
-template <int NW, bool FP8>
-__global__ __launch_bounds__(NW * 64) void mla_partial_kernel(MlaArgs a) {
-  using C = MlaCfg<NW, FP8>;
-  static_assert(kStages == 4, "wait_tiles_after assumes at most two tiles in flight after one");
+// Location of copy slot `slot` of a tile: row and logical 16-byte chunk.
+template <bool FP8>
+__device__ __forceinline__ void slot_row_chunk(int slot, int& row, int& c) {
+  if constexpr (FP8) {
+    row = slot / kF8RowCh;
+    c = slot - row * kF8RowCh;
+  } else {
+    row = slot / kRowCh;
+    const int pc = slot - row * kRowCh;
+    c = (pc & ~7) | ((pc & 7) ^ swz(row));
+  }
+}
+
+// BS32: every block holds a multiple of 32 tokens, so a tile lies inside one
+// block and its copies are a uniform base plus fixed per-lane offsets.
+template <int HG, bool FP8, bool BS32>
+__global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
+  using C = Cfg<HG, FP8>;
+  using E = Elt<FP8>;
+  constexpr int NW = C::NW;
+  constexpr int kMT = C::kMT;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::kLds];
   DCP_LDS char* smem = (DCP_LDS char*)smem_raw;
   DCP_LDS int* ids = (DCP_LDS int*)(smem + C::kIdsOff);
+  DCP_LDS float* mx = (DCP_LDS float*)(smem + C::kMxOff);
+  DCP_LDS float* lsum = (DCP_LDS float*)(smem + C::kLsumOff);
   DCP_LDS char* pad = smem + C::kPadOff;
+  const uint32_t smem_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  const int hg = w % HG;   // head group of this wave's scores
+  const int th = w / HG;   // token half of this wave's scores
   const int q4 = lane >> 4;
   const int l16 = lane & 15;
   const int g = xcd_logical_group(blockIdx.x, kGroups);
-  const int head0 = blockIdx.y * kHeadsPerGroup;
+  const int head0 = blockIdx.y * 16 * HG;
   const int chunk = a.hdr->chunk;
   const int total = a.hdr->total;
   int pos = g * chunk;
@@ -202,24 +264,35 @@ __global__ __launch_bounds__(NW * 64) void mla_partial_kernel(MlaArgs a) {
   if (pos >= end) return;
   int s = find_segment(a.seg_off, a.S, pos);
   const int bs = a.map.bs;
-  const int h = head0 + 16 * w + l16;
+  const int h_s = head0 + 16 * hg + l16;  // head of this lane's scores
 
-  // Per-lane constant LDS offsets.
-  // A fragment of S^T: rows l16 and 16 + l16, chunk 4kk + q4.
-  const int a_even0 = l16 * kRowB + 16 * (q4 ^ swz(l16));
-  const int a_odd0 = l16 * kRowB + 16 * ((4 + q4) ^ swz(l16));
-  const int a_even1 = (16 + l16) * kRowB + 16 * (q4 ^ swz(16 + l16));
-  const int a_odd1 = (16 + l16) * kRowB + 16 * ((4 + q4) ^ swz(16 + l16));
-  // Transposed A fragment of O^T: lane (k = l16/4, m = l16%4) points at rows
-  // 4q4 + k and 16 + 4q4 + k, bytes 32mt + 8m, i.e. chunk 2mt + m/2.
+  // ---- per-lane constant offsets
+  // S^T A fragment: row 16th + l16, chunk 4kk + q4 (even / odd kk).
+  const int a_row = 16 * th + l16;
+  const uint32_t a_even = a_row * kRowB + 16 * (q4 ^ swz(a_row));
+  const uint32_t a_odd = a_row * kRowB + 16 * ((4 + q4) ^ swz(a_row));
+  // O^T transposed A fragment: lane (k = l16/4, m = l16%4) points at rows
+  // 4q4 + k (tokens of half 0) and 16 + 4q4 + k (half 1), value columns
+  // v = vbase + 16mt + 4m .. +3, i.e. chunk vbase/8 + 2mt + m/2.
   const int t_k = l16 >> 2, t_m = l16 & 3;
   const int t_row0 = 4 * q4 + t_k, t_row1 = 16 + 4 * q4 + t_k;
-  int t_off0[4], t_off1[4];
+  const int vbase = 16 * kMT * w;
+  uint32_t t_off[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int c = 2 * j + (t_m >> 1);  // chunk within an aligned 8-chunk group
-    t_off0[j] = t_row0 * kRowB + 16 * (c ^ swz(t_row0)) + 8 * (t_m & 1);
-    t_off1[j] = t_row1 * kRowB + 16 * (c ^ swz(t_row1)) + 8 * (t_m & 1);
+    const int c = 2 * j + (t_m >> 1);
+    const int grp = 128 * (vbase / 64);  // the 8-chunk group holding value column vbase
+    t_off[j] = grp + t_row0 * kRowB + 16 * (c ^ swz(t_row0)) + 8 * (t_m & 1);
+    t_off[4 + j] = grp + t_row1 * kRowB + 16 * (c ^ swz(t_row1)) + 8 * (t_m & 1);
+  }
+  // Copy offsets of this lane within a tile (BS32 path).
+  int32_t cp_off[C::kPerWave];
+#pragma unroll
+  for (int n = 0; n < C::kPerWave; ++n) {
+    const int ii = w + NW * n;
+    int row = 0, c = 0;
+    if (ii < C::kInst) slot_row_chunk<FP8>(ii * 64 + lane, row, c);
+    cp_off[n] = static_cast<int32_t>(row * a.token_stride_b) + 16 * c;
   }
 
   while (pos < end) {
@@ -229,19 +302,24 @@ __global__ __launch_bounds__(NW * 64) void mla_partial_kernel(MlaArgs a) {
     const Piece p = make_piece(a.map, s, pos - seg_a, pe - seg_a);
     const int32_t* trow = a.map.table + static_cast<size_t>(p.b) * a.map.width;
 
-    // Query fragments (B operand of S^T): head h, columns 32kk + 8q4 .. +7.
-    typename Elt<FP8>::vec qf[kKSteps];
+    // Query fragments (B operand of S^T): head h_s, columns 32kk + 8q4 .. +7.
+    typename E::vec qf[kKSteps];
     {
-      const uint16_t* qrow = a.q + (static_cast<size_t>(p.b) * a.Hq + h) * kQK + 8 * q4;
+      const uint16_t* qrow = a.q + (static_cast<size_t>(p.b) * a.Hq + h_s) * kQK + 8 * q4;
 #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk)
-        qf[kk] = Elt<FP8>::from_bf16(*reinterpret_cast<const bf16x8*>(qrow + 32 * kk));
+        qf[kk] = E::from_bf16(*reinterpret_cast<const bf16x8*>(qrow + 32 * kk));
     }
-    f32x4 acc[kVTiles];
+    f32x4 acc[kMT][HG];
 #pragma unroll
-    for (int mt = 0; mt < kVTiles; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -INFINITY;  // reference max (log2 units) the accumulators are scaled to
-    float l_run = 0.f;
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < HG; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Reference max (log2 units) of heads 16nt + l16, identical in every wave.
+    float m_ref[HG];
+#pragma unroll
+    for (int nt = 0; nt < HG; ++nt) m_ref[nt] = -INFINITY;
+    float l_run = 0.f;  // sum of this lane's probabilities for head h_s
 
     // Windows of at most kIdWin blocks share one LDS copy of their block ids.
     for (int wb = p.i0; wb < p.i1; wb += kIdWin) {
@@ -253,63 +331,80 @@ __global__ __launch_bounds__(NW * 64) void mla_partial_kernel(MlaArgs a) {
       __syncthreads();
       const int ntiles = (ntok + kT - 1) / kT;
 
+      // Rows of tile j that hold real tokens with usable block ids.
+      auto valid_rows = [&](int j) -> unsigned long long {
+        const int tau0 = j * kT;
+        if constexpr (BS32) {
+          const int id = ids[tau0 / bs];
+          const int n = min(kT, ntok - tau0);
+          return (id >= 0 && id < a.ncb) ? ((1ull << n) - 1) : 0ull;
+        } else {
+          const int tau = tau0 + (lane & 31);
+          bool ok = lane < 32 && tau < ntok;
+          if (ok) {
+            const int id = ids[tau / bs];
+            ok = id >= 0 && id < a.ncb;
+          }
+          return __ballot(ok);
+        }
+      };
+
       // Copy tile j of this window into ring stage j % kStages. Every wave
       // issues exactly C::kOps vector-memory operations per tile.
       auto issue = [&](int j) {
         const int tau0 = j * kT;
         DCP_LDS char* dst = smem + (j % kStages) * C::kStageB;
-#pragma unroll 9
-        for (int n = 0; n < C::kPerWave; ++n) {
-          const int ii = w + NW * n;
-          const char* src;
-          DCP_LDS char* ldst;
-          if (ii < C::kInst) {
-            const int slot = ii * 64 + lane;
-            int row, c;
-            if constexpr (FP8) {
-              row = slot / kF8RowCh;
-              c = slot - row * kF8RowCh;
-            } else {
-              row = slot / kRowCh;
-              const int pc = slot - row * kRowCh;
-              c = (pc & ~7) | ((pc & 7) ^ swz(row));
-            }
-            const int tau = tau0 + row;
-            int id = tau < ntok ? ids[tau / bs] : -1;
-            src = a.kv + 16 * c;  // safe filler address (block 0, token 0)
-            if (id >= 0 && id < a.ncb)
-              src += static_cast<long long>(id) * a.block_stride_b +
-                     static_cast<long long>(tau % bs) * a.token_stride_b;
-            ldst = dst + ii * 1024;
-          } else {
-            src = a.kv;
-            ldst = pad;
+        if constexpr (BS32) {
+          // One block for the whole tile; an unusable id reads block 0 instead
+          // (the rows are zeroed after landing).
+          const int id = wave_uniform(ids[tau0 / bs]);
+          const char* base = a.kv;
+          if (id >= 0 && id < a.ncb)
+            base += static_cast<long long>(id) * a.block_stride_b +
+                    static_cast<long long>(tau0 % bs) * a.token_stride_b;
+#pragma unroll
+          for (int n = 0; n < C::kPerWave; ++n) {
+            const int ii = w + NW * n;
+            // (Operands bound to locals: with the expressions inline in the
+            // builtin's argument list the host pass drops this kernel's stub.)
+            const char* src = base + cp_off[n];
+            DCP_LDS char* ldst = ii < C::kInst ? dst + ii * 1024 : pad;
+            __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, 0);
           }
-          __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, 0);
+        } else {
+#pragma unroll
+          for (int n = 0; n < C::kPerWave; ++n) {
+            const int ii = w + NW * n;
+            const char* src = a.kv;
+            DCP_LDS char* ldst = pad;
+            if (ii < C::kInst) {
+              int row, c;
+              slot_row_chunk<FP8>(ii * 64 + lane, row, c);
+              src = a.kv + 16 * c;  // safe filler address (block 0, token 0)
+              const int tau = tau0 + row;
+              const int id = tau < ntok ? ids[tau / bs] : -1;
+              if (id >= 0 && id < a.ncb)
+                src += static_cast<long long>(id) * a.block_stride_b +
+                       static_cast<long long>(tau % bs) * a.token_stride_b;
+              ldst = dst + ii * 1024;
+            }
+            __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, 0);
+          }
         }
         if constexpr (FP8) {
+          // Wave 0 copies the tile's 32 token scales; the others pad their count.
           const int tau = tau0 + (lane & 31);
           const int id = tau < ntok ? ids[tau / bs] : -1;
           const char* src = a.kv_scale;
           if (id >= 0 && id < a.ncb) src += 4 * (static_cast<long long>(id) * bs + tau % bs);
           __builtin_amdgcn_global_load_lds(
-              src, smem + C::kScaleOff + ((j % kStages) * NW + w) * kScaleB, 4, 0, 0);
+              src, w == 0 ? smem + C::kScaleOff + (j % kStages) * 256 : pad, 4, 0, 0);
         }
-      };
-      // Rows of tile j that hold real tokens with usable block ids.
-      auto valid_rows = [&](int j) -> unsigned long long {
-        const int tau = j * kT + (lane & 31);
-        bool ok = lane < 32 && tau < ntok;
-        if (ok) {
-          const int id = ids[tau / bs];
-          ok = id >= 0 && id < a.ncb;
-        }
-        return __ballot(ok);
       };
       // fp8 tile j -> the fp16 tile the MFMAs read (buffer j & 1).
       auto widen = [&](int j, unsigned long long vm) {
         const DCP_LDS char* stg = smem + (j % kStages) * kF8TileB;
-        DCP_LDS char* dstb = smem + C::kBf16Off + (j & 1) * kTileB;
+        DCP_LDS char* dstb = smem + C::kF16Off + (j & 1) * kTileB;
         for (int u = threadIdx.x; u < kTileCh; u += NW * 64) {
           const int row = u / kRowCh;
           const int c = u - row * kRowCh;
@@ -329,17 +424,17 @@ __global__ __launch_bounds__(NW * 64) void mla_partial_kernel(MlaArgs a) {
       unsigned long long vm_next = 0;
       if constexpr (FP8) {
         // Widen tile 0 before the loop; tile k + 1 is widened while tile k is consumed.
-        wait_tiles_after<NW, FP8>(min(kStages - 2, ntiles - 1));
+        wait_tiles_after<C>(min(kStages - 2, ntiles - 1));
         __syncthreads();
         widen(0, valid_rows(0));
         if (ntiles > 1) vm_next = valid_rows(1);
       }
 
       for (int k = 0; k < ntiles; ++k) {
-        const DCP_LDS char* tile;
+        uint32_t tile;
         unsigned long long vm_k;
         if constexpr (!FP8) {
-          wait_tiles_after<NW, FP8>(min(kStages - 2, ntiles - 1 - k));
+          wait_tiles_after<C>(min(kStages - 2, ntiles - 1 - k));
           vm_k = valid_rows(k);
           if (vm_k != 0xffffffffull) {
             // Zero the rows that were filled from the safe address, once every
@@ -352,104 +447,150 @@ __global__ __launch_bounds__(NW * 64) void mla_partial_kernel(MlaArgs a) {
           }
           __syncthreads();
           if (k + kStages - 1 < ntiles) issue(k + kStages - 1);
-          tile = smem + (k % kStages) * kTileB;
+          tile = smem_addr + (k % kStages) * kTileB;
         } else {
           // Tile k is already widened (previous iteration or prologue).
           vm_k = k == 0 ? valid_rows(0) : vm_next;
           if (k + 1 < ntiles) {
-            wait_tiles_after<NW, FP8>(min(1, ntiles - 2 - k));
+            wait_tiles_after<C>(min(1, ntiles - 2 - k));
             vm_next = valid_rows(k + 1);
           }
           __syncthreads();
           if (k + kStages - 1 < ntiles) issue(k + kStages - 1);
           if (k + 1 < ntiles) widen(k + 1, vm_next);
-          tile = smem + C::kBf16Off + (k & 1) * kTileB;
+          tile = smem_addr + C::kF16Off + (k & 1) * kTileB;
         }
 
-        // ---- S^T = C_tile . Q^T : two 16-token M tiles, 18 K steps of 32 columns
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < kKSteps; ++kk) {
-          const int base = 128 * (kk >> 1);
-          const auto a0 = __builtin_bit_cast(typename Elt<FP8>::vec,
-              lds_read_b128(tile + ((kk & 1) ? a_odd0 : a_even0) + base));
-          const auto a1 = __builtin_bit_cast(typename Elt<FP8>::vec,
-              lds_read_b128(tile + ((kk & 1) ? a_odd1 : a_even1) + base));
-          s0 = Elt<FP8>::mfma(a0, qf[kk], s0);
-          s1 = Elt<FP8>::mfma(a1, qf[kk], s1);
-        }
+        // ---- S^T for the 16 tokens of half th and heads of group hg: 18 K steps,
+        // A fragments read kSDist steps ahead, two accumulator chains.
+        const uint32_t ae = tile + a_even, ao = tile + a_odd;
+        i32x4 ra[kSRing];
+        auto s_issue = [&](auto kc) {
+          constexpr int kk = decltype(kc)::value;
+          constexpr int off = 128 * (kk >> 1);
+          if constexpr (kk & 1) lds_b128<off>(ra[kk % kSRing], ao);
+          else lds_b128<off>(ra[kk % kSRing], ae);
+        };
+        static_for<0, kSDist>(s_issue);
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+        static_for<0, kKSteps>([&](auto kc) {
+          constexpr int kk = decltype(kc)::value;
+          if constexpr (kk + kSDist < kKSteps) s_issue(IC<kk + kSDist>{});
+          constexpr int ahead = kk + kSDist < kKSteps ? kSDist : kKSteps - 1 - kk;
+          wait_lgkm<ahead>(ra[kk % kSRing]);
+          if constexpr (kk & 1) sb = E::mfma(ra[kk % kSRing], qf[kk], sb);
+          else sa = E::mfma(ra[kk % kSRing], qf[kk], sa);
+        });
+        const f32x4 sv = sa + sb;
 
-        // ---- online softmax for head h over tokens 4q4+i and 16+4q4+i
-        float x[8], sig[8];
-        const DCP_LDS float* sc =
-            (const DCP_LDS float*)(smem + C::kScaleOff + ((k % kStages) * NW + w) * kScaleB);
+        // ---- softmax, part 1: this half's max per head, exchanged through LDS
+        float x[4], sig[4];
+        const DCP_LDS float* sc = (const DCP_LDS float*)(smem + C::kScaleOff + (k % kStages) * 256);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r0 = 4 * q4 + i, r1 = 16 + 4 * q4 + i;
-          sig[i] = FP8 ? sc[r0] : 1.f;
-          sig[4 + i] = FP8 ? sc[r1] : 1.f;
-          x[i] = ((vm_k >> r0) & 1ull) ? s0[i] * sig[i] * a.scale_log2 : -INFINITY;
-          x[4 + i] = ((vm_k >> r1) & 1ull) ? s1[i] * sig[4 + i] * a.scale_log2 : -INFINITY;
+          const int r = 16 * th + 4 * q4 + i;
+          sig[i] = FP8 ? sc[r] : 1.f;
+          x[i] = ((vm_k >> r) & 1ull) ? sv[i] * sig[i] * a.scale_log2 : -INFINITY;
         }
-        float tmax = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        // bf16 cache: probabilities may reach 2^8 before a rescale. fp8 cache:
-        // rescale on any increase, so p <= 1 and p * scale stays in fp16 range.
-        const bool raise = tmax > m_ref + (FP8 ? 0.f : 8.f);
-        float alpha = 1.f;
-        if (raise) {
-          alpha = fast_exp2(m_ref - tmax);  // 0 on the first tile (m_ref = -inf)
-          m_ref = tmax;
-        }
-        if (__ballot(raise)) {
-#pragma unroll
-          for (int mt = 0; mt < kVTiles; ++mt) acc[mt] *= alpha;
-          l_run *= alpha;
-        }
-        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-        float psum = 0.f;
-        uint32_t pk[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = fast_exp2(x[2 * i] - m_use);
-          const float p1 = fast_exp2(x[2 * i + 1] - m_use);
-          const uint16_t b0 = Elt<FP8>::from_f32(FP8 ? p0 * sig[2 * i] : p0);
-          const uint16_t b1 = Elt<FP8>::from_f32(FP8 ? p1 * sig[2 * i + 1] : p1);
-          psum += p0 + p1;  // the normaliser keeps the fp32 probabilities
-          pk[i] = static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16);
-        }
-        l_run += psum;
-        const i32x4 pki = {static_cast<int>(pk[0]), static_cast<int>(pk[1]),
-                           static_cast<int>(pk[2]), static_cast<int>(pk[3])};
-        const auto pb = __builtin_bit_cast(typename Elt<FP8>::vec, pki);
+        float hmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        hmax = fmaxf(hmax, __shfl_xor(hmax, 16));
+        hmax = fmaxf(hmax, __shfl_xor(hmax, 32));
+        if (q4 == 0) mx[(th * 16 + l16) * 4 + hg] = hmax;
+        __syncthreads();
 
-        // ---- O^T += C_tile^T . P^T : 32 M tiles of 16 value columns, one K step
+        // ---- part 2: every wave updates the reference max of heads 16nt + l16
+        float alpha[HG];
+        bool any_raise = false;
+        {
+          const f32x4 m0 = *reinterpret_cast<const DCP_LDS f32x4*>(mx + l16 * 4);
+          const f32x4 m1 = *reinterpret_cast<const DCP_LDS f32x4*>(mx + (16 + l16) * 4);
 #pragma unroll
-        for (int mt = 0; mt < kVTiles; ++mt) {
-          const int base = 128 * (mt >> 2);
-          const s16x4 lo = lds_read_tr(tile + t_off0[mt & 3] + base);
-          const s16x4 hi = lds_read_tr(tile + t_off1[mt & 3] + base);
-          const short __attribute__((ext_vector_type(8))) cat = {lo[0], lo[1], lo[2], lo[3],
-                                                                 hi[0], hi[1], hi[2], hi[3]};
-          acc[mt] = Elt<FP8>::mfma(__builtin_bit_cast(typename Elt<FP8>::vec, cat), pb, acc[mt]);
+          for (int nt = 0; nt < HG; ++nt) {
+            const float tmax = fmaxf(m0[nt], m1[nt]);
+            // bf16 cache: probabilities may reach 2^8 before a rescale. fp8
+            // cache: rescale on any increase, so p <= 1 and p * scale stays
+            // inside the fp16 range.
+            const bool raise = tmax > m_ref[nt] + (FP8 ? 0.f : 8.f);
+            alpha[nt] = raise ? fast_exp2(m_ref[nt] - tmax) : 1.f;  // 0 when m_ref = -inf
+            m_ref[nt] = raise ? tmax : m_ref[nt];
+            any_raise |= raise;
+          }
         }
+        float m_own = m_ref[0], a_own = alpha[0];
+#pragma unroll
+        for (int nt = 1; nt < HG; ++nt)
+          if (nt == hg) { m_own = m_ref[nt]; a_own = alpha[nt]; }
+        const float m_use = m_own == -INFINITY ? 0.f : m_own;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m_use);
+        l_run = l_run * a_own + ((p[0] + p[1]) + (p[2] + p[3]));
+        // P^T fragment half of this wave: tokens 16th + 4q4 + i of head h_s.
+        {
+          const uint32_t lo = E::pack2(FP8 ? p[0] * sig[0] : p[0], FP8 ? p[1] * sig[1] : p[1]);
+          const uint32_t hi = E::pack2(FP8 ? p[2] * sig[2] : p[2], FP8 ? p[3] * sig[3] : p[3]);
+          *reinterpret_cast<DCP_LDS i32x2*>(smem + C::kPOff + ((hg * 64 + lane) * 2 + th) * 8) =
+              i32x2{static_cast<int>(lo), static_cast<int>(hi)};
+        }
+        __syncthreads();
+
+        // ---- O^T += C_tile^T . P^T over this wave's value slice, all head groups
+        if (__ballot(any_raise)) {
+#pragma unroll
+          for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < HG; ++nt) acc[mt][nt] *= alpha[nt];
+        }
+        i32x4 pb[HG];
+        const uint32_t pbase = smem_addr + C::kPOff + lane * 16;
+        static_for<0, HG>([&](auto nc) {
+          constexpr int nt = decltype(nc)::value;
+          lds_b128<nt * 1024>(pb[nt], pbase);
+        });
+        uint32_t tb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tb[j] = tile + t_off[j];
+        constexpr int kPD = kMT < 4 ? kMT : 4;  // M tiles of transposed reads in flight
+        i32x2 rlo[kPD + 2], rhi[kPD + 2];
+        auto p_issue = [&](auto mc) {
+          constexpr int mt = decltype(mc)::value;
+          constexpr int off = 128 * (mt >> 2);
+          lds_tr<off>(rlo[mt % (kPD + 2)], tb[mt & 3]);
+          lds_tr<off>(rhi[mt % (kPD + 2)], tb[4 + (mt & 3)]);
+        };
+        static_for<0, kPD>(p_issue);
+        static_for<0, kMT>([&](auto mc) {
+          constexpr int mt = decltype(mc)::value;
+          if constexpr (mt + kPD < kMT) p_issue(IC<mt + kPD>{});
+          constexpr int ahead = mt + kPD < kMT ? kPD : kMT - 1 - mt;
+          wait_lgkm<2 * ahead>(rlo[mt % (kPD + 2)], rhi[mt % (kPD + 2)]);
+          const i32x4 av = {rlo[mt % (kPD + 2)][0], rlo[mt % (kPD + 2)][1],
+                            rhi[mt % (kPD + 2)][0], rhi[mt % (kPD + 2)][1]};
+          static_for<0, HG>([&](auto nc) {
+            constexpr int nt = decltype(nc)::value;
+            acc[mt][nt] = E::mfma(av, __builtin_bit_cast(typename E::vec, pb[nt]), acc[mt][nt]);
+          });
+        });
       }
       __syncthreads();  // ring stages and ids are reused by the next window / piece
     }
 
     // ---- finalise the piece: normalise and store (O, LSE) in slot s + g
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    float l_h = l_run + __shfl_xor(l_run, 16);
+    l_h += __shfl_xor(l_h, 32);
+    if (q4 == 0) lsum[th * 64 + 16 * hg + l16] = l_h;
+    __syncthreads();
     const size_t slot = static_cast<size_t>(s) + g;
-    float* orow = a.ws_o + (slot * a.Hq + h) * kV + 4 * q4;
 #pragma unroll
-    for (int mt = 0; mt < kVTiles; ++mt) *reinterpret_cast<f32x4*>(orow + 16 * mt) = acc[mt] * inv;
-    if (q4 == 0) a.ws_lse[slot * a.Hq + h] = lse;
+    for (int nt = 0; nt < HG; ++nt) {
+      const float l_tot = lsum[16 * nt + l16] + lsum[64 + 16 * nt + l16];
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) *reinterpret_cast<f32x4*>(orow + 16 * mt) = acc[mt][nt] * inv;
+      if (th == 0 && nt == hg && q4 == 0)
+        a.ws_lse[slot * a.Hq + h_s] = l_tot > 0.f ? (m_ref[nt] + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    }
     pos = pe;
   }
 }
@@ -464,6 +605,14 @@ bool mla_supported(const dcp_attn_desc_t* d) {
          (d->kv_dtype == DCP_BF16 || d->kv_dtype == DCP_FP8_E4M3) &&
          (d->num_q_heads == 16 || d->num_q_heads == 32 || d->num_q_heads % 64 == 0) &&
          d->num_q_heads <= 256;
+}
+
+template <int HG, bool FP8>
+static void launch_mla_hg(const MlaArgs& a, bool bs32, dim3 grid, hipStream_t stream) {
+  if (bs32)
+    hipLaunchKernelGGL((mla_partial_kernel<HG, FP8, true>), grid, dim3(2 * HG * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((mla_partial_kernel<HG, FP8, false>), grid, dim3(2 * HG * 64), 0, stream, a);
 }
 
 hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
@@ -485,24 +634,27 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   a.Hq = d->num_q_heads;
   a.scale_log2 = d->softmax_scale * kLog2e;
   const bool fp8 = d->kv_dtype == DCP_FP8_E4M3;
-  const int heads = d->num_q_heads < kHeadsPerGroup ? d->num_q_heads : kHeadsPerGroup;
-  const int nw = heads / 16;
+  // A tile of 32 tokens lies inside one block when blocks hold a multiple of
+  // 32 tokens; per-lane copy offsets (row * token stride) then fit in 32 bits.
+  const bool bs32 = d->block_size % kT == 0 && a.token_stride_b * kT < (1ll << 30);
+  const int heads = d->num_q_heads < 64 ? d->num_q_heads : 64;
   const dim3 grid(kGroups, d->num_q_heads / heads);
-#define DCP_MLA_CASE(NW_)                                                                     \
-  case NW_:                                                                                   \
-    if (fp8)                                                                                  \
-      hipLaunchKernelGGL((mla_partial_kernel<NW_, true>), grid, dim3(NW_ * 64), 0, stream, a); \
-    else                                                                                      \
-      hipLaunchKernelGGL((mla_partial_kernel<NW_, false>), grid, dim3(NW_ * 64), 0, stream, a); \
-    break;
-  switch (nw) {
-    DCP_MLA_CASE(1)
-    DCP_MLA_CASE(2)
-    DCP_MLA_CASE(4)
+  switch (heads / 16) {
+    case 1:
+      if (fp8) launch_mla_hg<1, true>(a, bs32, grid, stream);
+      else launch_mla_hg<1, false>(a, bs32, grid, stream);
+      break;
+    case 2:
+      if (fp8) launch_mla_hg<2, true>(a, bs32, grid, stream);
+      else launch_mla_hg<2, false>(a, bs32, grid, stream);
+      break;
+    case 4:
+      if (fp8) launch_mla_hg<4, true>(a, bs32, grid, stream);
+      else launch_mla_hg<4, false>(a, bs32, grid, stream);
+      break;
     default:
       return hipErrorInvalidValue;
   }
-#undef DCP_MLA_CASE
   return hipGetLastError();
 }
 

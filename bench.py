@@ -67,10 +67,12 @@ def cpu_baseline(w, o_gpu, lse_gpu, budget_s: float):
     from threadpoolctl import threadpool_info
 
     order = np.argsort(w.seq_lens, kind="stable")
-    # Stratified over the sorted lengths: every 8th sequence, starting in the middle of
-    # each group of 8, visited from the middle of the length range outwards.
-    picks = [int(order[i]) for i in range(4, len(order), 8)]
-    picks.sort(key=lambda b: abs(int(np.where(order == b)[0][0]) - len(order) // 2))
+    # Stratified over the sorted lengths: passes over every 8th sequence, each pass
+    # starting at a different offset inside the groups of 8, so that any prefix of the
+    # visit order spans the whole length range. Stops once the budget is spent or
+    # every sequence was visited.
+    picks = [int(order[i]) for off in (4, 0, 6, 2, 5, 1, 7, 3)
+             for i in range(off, len(order), 8)]
     done, tokens, t_used = [], 0, 0.0
     errs = []
     for b in picks:

@@ -113,6 +113,10 @@ __device__ __forceinline__ void lds_b128(i32x4& r, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
 }
 template <int OFF>
+__device__ __forceinline__ void lds_b64(i32x2& r, uint32_t addr) {
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
 __device__ __forceinline__ void lds_tr(i32x2& r, uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
 }
@@ -125,6 +129,15 @@ __device__ __forceinline__ void wait_lgkm(T0& a) {
 template <int N, class T0, class T1>
 __device__ __forceinline__ void wait_lgkm(T0& a, T1& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+
+// Work-group barrier that orders LDS accesses only. __syncthreads() also
+// completes every earlier memory operation of the wave, which includes the
+// direct-to-LDS copies still in flight, so it would drain the prefetch
+// pipeline at every barrier. Here each wave waits for its own LDS accesses;
+// copy completion is awaited explicitly (wait_vm) before a tile is read.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // A value every lane holds identically, moved to a scalar register.
@@ -193,17 +206,21 @@ struct Cfg {
   static constexpr int kPerWave = (kInst + NW - 1) / NW;      // tile copies per wave
   static constexpr int kOps = kPerWave + (FP8 ? 1 : 0);        // + the scale copy
   static constexpr int kStageB = FP8 ? kF8TileB : kTileB;
-  // LDS layout
-  static constexpr int kRingOff = 0;
-  static constexpr int kF16Off = kStages * kF8TileB;          // fp8: two fp16 tiles
-  static constexpr int kScaleOff = kF16Off + 2 * kTileB;       // fp8: kStages x 256 B
-  static constexpr int kPOff = FP8 ? kScaleOff + kStages * 256 : kStages * kTileB;
+  // LDS is two arrays. The copies write only `ring` (tile stages, fp8 scales,
+  // the filler pad); everything the waves store themselves lives in `aux`.
+  // As separate objects the compiler can prove that a store to or a load from
+  // `aux` never aliases an in-flight copy, so it adds no wait for the copies
+  // before such accesses (which would drain the whole prefetch pipeline).
+  static constexpr int kScaleOff = kStages * kStageB;          // fp8: kStages x 256 B
+  static constexpr int kPadOff = kScaleOff + (FP8 ? kStages * 256 : 0);
+  static constexpr int kRingB = kPadOff + kPadB;
+  static constexpr int kF16Off = 0;                            // fp8: two fp16 tiles
+  static constexpr int kPOff = FP8 ? 2 * kTileB : 0;
   static constexpr int kMxOff = kPOff + HG * 64 * 16;          // [2][16][4] floats
   static constexpr int kLsumOff = kMxOff + 2 * 16 * 4 * 4;     // [2][64] floats
   static constexpr int kIdsOff = kLsumOff + 2 * 64 * 4;
-  static constexpr int kPadOff = kIdsOff + kIdWin * 4;
-  static constexpr int kLds = kPadOff + kPadB;
-  static_assert(kLds <= 160 * 1024, "LDS budget");
+  static constexpr int kAuxB = kIdsOff + kIdWin * 4;
+  static_assert(kRingB + kAuxB <= 160 * 1024, "LDS budget");
 };
 
 // Wait until at most n_after tiles (C::kOps operations each) issued after the
@@ -241,13 +258,16 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
   using E = Elt<FP8>;
   constexpr int NW = C::NW;
   constexpr int kMT = C::kMT;
-  __shared__ __attribute__((aligned(16))) char smem_raw[C::kLds];
-  DCP_LDS char* smem = (DCP_LDS char*)smem_raw;
-  DCP_LDS int* ids = (DCP_LDS int*)(smem + C::kIdsOff);
-  DCP_LDS float* mx = (DCP_LDS float*)(smem + C::kMxOff);
-  DCP_LDS float* lsum = (DCP_LDS float*)(smem + C::kLsumOff);
-  DCP_LDS char* pad = smem + C::kPadOff;
-  const uint32_t smem_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+  __shared__ __attribute__((aligned(16))) char ring_raw[C::kRingB];
+  __shared__ __attribute__((aligned(16))) char aux_raw[C::kAuxB];
+  DCP_LDS char* ring = (DCP_LDS char*)ring_raw;
+  DCP_LDS char* aux = (DCP_LDS char*)aux_raw;
+  DCP_LDS int* ids = (DCP_LDS int*)(aux + C::kIdsOff);
+  DCP_LDS float* mx = (DCP_LDS float*)(aux + C::kMxOff);
+  DCP_LDS float* lsum = (DCP_LDS float*)(aux + C::kLsumOff);
+  DCP_LDS char* pad = ring + C::kPadOff;
+  const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+  const uint32_t aux_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aux));
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -353,7 +373,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
       // issues exactly C::kOps vector-memory operations per tile.
       auto issue = [&](int j) {
         const int tau0 = j * kT;
-        DCP_LDS char* dst = smem + (j % kStages) * C::kStageB;
+        DCP_LDS char* dst = ring + (j % kStages) * C::kStageB;
         if constexpr (BS32) {
           // One block for the whole tile; an unusable id reads block 0 instead
           // (the rows are zeroed after landing).
@@ -398,19 +418,21 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
           const char* src = a.kv_scale;
           if (id >= 0 && id < a.ncb) src += 4 * (static_cast<long long>(id) * bs + tau % bs);
           __builtin_amdgcn_global_load_lds(
-              src, w == 0 ? smem + C::kScaleOff + (j % kStages) * 256 : pad, 4, 0, 0);
+              src, w == 0 ? ring + C::kScaleOff + (j % kStages) * 256 : pad, 4, 0, 0);
         }
       };
       // fp8 tile j -> the fp16 tile the MFMAs read (buffer j & 1).
       auto widen = [&](int j, unsigned long long vm) {
-        const DCP_LDS char* stg = smem + (j % kStages) * kF8TileB;
-        DCP_LDS char* dstb = smem + C::kF16Off + (j & 1) * kTileB;
+        const uint32_t stg = ring_addr + (j % kStages) * kF8TileB;
+        DCP_LDS char* dstb = aux + C::kF16Off + (j & 1) * kTileB;
         for (int u = threadIdx.x; u < kTileCh; u += NW * 64) {
           const int row = u / kRowCh;
           const int c = u - row * kRowCh;
           i32x4 wv = {0, 0, 0, 0};
           if ((vm >> row) & 1ull) {
-            const i32x2 codes = *reinterpret_cast<const DCP_LDS i32x2*>(stg + row * kF8RowB + 8 * c);
+            i32x2 codes;
+            lds_b64<0>(codes, stg + row * kF8RowB + 8 * c);
+            wait_lgkm<0>(codes);
             wv[0] = static_cast<int>(f8x2_to_f16x2<false>(static_cast<uint32_t>(codes[0])));
             wv[1] = static_cast<int>(f8x2_to_f16x2<true>(static_cast<uint32_t>(codes[0])));
             wv[2] = static_cast<int>(f8x2_to_f16x2<false>(static_cast<uint32_t>(codes[1])));
@@ -425,7 +447,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
       if constexpr (FP8) {
         // Widen tile 0 before the loop; tile k + 1 is widened while tile k is consumed.
         wait_tiles_after<C>(min(kStages - 2, ntiles - 1));
-        __syncthreads();
+        lds_barrier();
         widen(0, valid_rows(0));
         if (ntiles > 1) vm_next = valid_rows(1);
       }
@@ -439,15 +461,15 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
           if (vm_k != 0xffffffffull) {
             // Zero the rows that were filled from the safe address, once every
             // wave's copies of this tile have landed.
-            __syncthreads();
-            DCP_LDS char* st = smem + (k % kStages) * kTileB;
+            lds_barrier();
+            DCP_LDS char* st = ring + (k % kStages) * kTileB;
             for (int u = threadIdx.x; u < kTileCh; u += NW * 64)
               if (!((vm_k >> (u / kRowCh)) & 1ull))
                 *reinterpret_cast<DCP_LDS i32x4*>(st + 16 * u) = i32x4{0, 0, 0, 0};
           }
-          __syncthreads();
+          lds_barrier();
           if (k + kStages - 1 < ntiles) issue(k + kStages - 1);
-          tile = smem_addr + (k % kStages) * kTileB;
+          tile = ring_addr + (k % kStages) * kTileB;
         } else {
           // Tile k is already widened (previous iteration or prologue).
           vm_k = k == 0 ? valid_rows(0) : vm_next;
@@ -455,10 +477,10 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
             wait_tiles_after<C>(min(1, ntiles - 2 - k));
             vm_next = valid_rows(k + 1);
           }
-          __syncthreads();
+          lds_barrier();
           if (k + kStages - 1 < ntiles) issue(k + kStages - 1);
           if (k + 1 < ntiles) widen(k + 1, vm_next);
-          tile = smem_addr + C::kF16Off + (k & 1) * kTileB;
+          tile = aux_addr + C::kF16Off + (k & 1) * kTileB;
         }
 
         // ---- S^T for the 16 tokens of half th and heads of group hg: 18 K steps,
@@ -485,18 +507,26 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
 
         // ---- softmax, part 1: this half's max per head, exchanged through LDS
         float x[4], sig[4];
-        const DCP_LDS float* sc = (const DCP_LDS float*)(smem + C::kScaleOff + (k % kStages) * 256);
+        f32x4 sc4 = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (FP8) {
+          // The four token scales of this lane's score rows (copied by the engine,
+          // so read with an explicit wait rather than a plain load).
+          i32x4 raw;
+          lds_b128<0>(raw, ring_addr + C::kScaleOff + (k % kStages) * 256 + 4 * (16 * th + 4 * q4));
+          wait_lgkm<0>(raw);
+          sc4 = __builtin_bit_cast(f32x4, raw);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * th + 4 * q4 + i;
-          sig[i] = FP8 ? sc[r] : 1.f;
+          sig[i] = sc4[i];
           x[i] = ((vm_k >> r) & 1ull) ? sv[i] * sig[i] * a.scale_log2 : -INFINITY;
         }
         float hmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         hmax = fmaxf(hmax, __shfl_xor(hmax, 16));
         hmax = fmaxf(hmax, __shfl_xor(hmax, 32));
         if (q4 == 0) mx[(th * 16 + l16) * 4 + hg] = hmax;
-        __syncthreads();
+        lds_barrier();
 
         // ---- part 2: every wave updates the reference max of heads 16nt + l16
         float alpha[HG];
@@ -529,10 +559,10 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
         {
           const uint32_t lo = E::pack2(FP8 ? p[0] * sig[0] : p[0], FP8 ? p[1] * sig[1] : p[1]);
           const uint32_t hi = E::pack2(FP8 ? p[2] * sig[2] : p[2], FP8 ? p[3] * sig[3] : p[3]);
-          *reinterpret_cast<DCP_LDS i32x2*>(smem + C::kPOff + ((hg * 64 + lane) * 2 + th) * 8) =
+          *reinterpret_cast<DCP_LDS i32x2*>(aux + C::kPOff + ((hg * 64 + lane) * 2 + th) * 8) =
               i32x2{static_cast<int>(lo), static_cast<int>(hi)};
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- O^T += C_tile^T . P^T over this wave's value slice, all head groups
         if (__ballot(any_raise)) {
@@ -542,7 +572,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
             for (int nt = 0; nt < HG; ++nt) acc[mt][nt] *= alpha[nt];
         }
         i32x4 pb[HG];
-        const uint32_t pbase = smem_addr + C::kPOff + lane * 16;
+        const uint32_t pbase = aux_addr + C::kPOff + lane * 16;
         static_for<0, HG>([&](auto nc) {
           constexpr int nt = decltype(nc)::value;
           lds_b128<nt * 1024>(pb[nt], pbase);

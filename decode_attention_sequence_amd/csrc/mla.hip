@@ -112,6 +112,9 @@ template <int OFF>
 __device__ __forceinline__ void lds_b128(i32x4& r, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
 }
+__device__ __forceinline__ void lds_store_b8(uint32_t addr, int v) {
+  asm volatile("ds_write_b8 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
 template <int OFF>
 __device__ __forceinline__ void lds_b64(i32x2& r, uint32_t addr) {
   asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
@@ -138,6 +141,27 @@ __device__ __forceinline__ void wait_lgkm(T0& a, T1& b) {
 // copy completion is awaited explicitly (wait_vm) before a tile is read.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The value held by the lane 16 (or 32) positions away, through the gfx950
+// row-swap permutes (plain VALU, no LDS round trip). With both operands set to
+// x, the swap returns x of this lane and x of its partner in some order, so
+// only symmetric combinations (max, sum) are formed from the pair.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // A value every lane holds identically, moved to a scalar register.
@@ -203,8 +227,14 @@ struct Cfg {
   static constexpr int NW = 2 * HG;
   static constexpr int kMT = 32 / NW;                          // value M tiles per wave
   static constexpr int kInst = FP8 ? kF8DmaInst : kDmaInst;
-  static constexpr int kPerWave = (kInst + NW - 1) / NW;      // tile copies per wave
-  static constexpr int kOps = kPerWave + (FP8 ? 1 : 0);        // + the scale copy
+  static constexpr int kPerWave = (kInst + NW - 1) / NW;      // tile copies per wave (at most)
+  // Vector-memory operations per tile of a wave with kPerWave copies and of
+  // one with a copy fewer (bf16: the last round of copies covers only the first
+  // kInst % NW waves). The fp8 path keeps one count: its waves all issue
+  // kPerWave copies (the surplus ones land in the pad) plus the scale copy.
+  static constexpr int kOpsHi = kPerWave + (FP8 ? 1 : 0);
+  static constexpr int kOpsLo = (FP8 || kInst % NW == 0) ? kOpsHi : kOpsHi - 1;
+  static constexpr int kHiWaves = (FP8 || kInst % NW == 0) ? NW : kInst % NW;
   static constexpr int kStageB = FP8 ? kF8TileB : kTileB;
   // LDS is two arrays. The copies write only `ring` (tile stages, fp8 scales,
   // the filler pad); everything the waves store themselves lives in `aux`.
@@ -219,17 +249,18 @@ struct Cfg {
   static constexpr int kMxOff = kPOff + HG * 64 * 16;          // [2][16][4] floats
   static constexpr int kLsumOff = kMxOff + 2 * 16 * 4 * 4;     // [2][64] floats
   static constexpr int kIdsOff = kLsumOff + 2 * 64 * 4;
-  static constexpr int kAuxB = kIdsOff + kIdWin * 4;
+  static constexpr int kFlagOff = kIdsOff + kIdWin * 4;        // one byte per wave
+  static constexpr int kAuxB = kFlagOff + 16;
   static_assert(kRingB + kAuxB <= 160 * 1024, "LDS budget");
 };
 
 // Wait until at most n_after tiles (C::kOps operations each) issued after the
 // awaited one are still in flight. The hardware counter saturates at 63, so
 // larger counts are clamped, which only waits for more.
-template <class C>
-__device__ __forceinline__ void wait_tiles_after(int n_after) {
-  constexpr int k1 = C::kOps > 63 ? 63 : C::kOps;
-  constexpr int k2 = 2 * C::kOps > 63 ? 63 : 2 * C::kOps;
+template <int OPS>
+__device__ __forceinline__ void wait_tiles_after_n(int n_after) {
+  constexpr int k1 = OPS > 63 ? 63 : OPS;
+  constexpr int k2 = 2 * OPS > 63 ? 63 : 2 * OPS;
   switch (n_after) {
     case 0: wait_vm<0>(); break;
     case 1: wait_vm<k1>(); break;
@@ -270,7 +301,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
   const uint32_t aux_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aux));
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = wave_uniform(threadIdx.x >> 6);
   const int hg = w % HG;   // head group of this wave's scores
   const int th = w / HG;   // token half of this wave's scores
   const int q4 = lane >> 4;
@@ -285,6 +316,13 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
   int s = find_segment(a.seg_off, a.S, pos);
   const int bs = a.map.bs;
   const int h_s = head0 + 16 * hg + l16;  // head of this lane's scores
+  const uint32_t flags_addr = aux_addr + C::kFlagOff;
+  // Wait for the copies of a tile, given how many tiles were issued after it.
+  const bool hi_wave = w < C::kHiWaves;
+  auto wait_tiles = [&](int n_after) {
+    if (hi_wave) wait_tiles_after_n<C::kOpsHi>(n_after);
+    else wait_tiles_after_n<C::kOpsLo>(n_after);
+  };
 
   // ---- per-lane constant offsets
   // S^T A fragment: row 16th + l16, chunk 4kk + q4 (even / odd kk).
@@ -315,6 +353,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
     cp_off[n] = static_cast<int32_t>(row * a.token_stride_b) + 16 * c;
   }
 
+  if (threadIdx.x < 16) aux[C::kFlagOff + threadIdx.x] = 0;  // unused vote bytes stay 0
   while (pos < end) {
     while (a.seg_off[s + 1] <= pos) ++s;
     const int seg_a = a.seg_off[s];
@@ -369,32 +408,43 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
         }
       };
 
+      // BS32: source of tile j, one block for the whole tile. An unusable id
+      // reads block 0 instead (the rows are zeroed after landing).
+      auto tile_src = [&](int j) -> const char* {
+        const int tau0 = j * kT;
+        const int id = wave_uniform(ids[tau0 / bs]);
+        const char* base = a.kv;
+        if (id >= 0 && id < a.ncb)
+          base += static_cast<long long>(id) * a.block_stride_b +
+                  static_cast<long long>(tau0 % bs) * a.token_stride_b;
+        return base;
+      };
+      // BS32: copy n of this wave for tile j (16 bytes per lane). A bf16 wave
+      // whose last round falls past the tile skips it; fp8 waves send it to the pad.
+      auto copy_one = [&](auto nc, const char* base, int j) {
+        constexpr int n = decltype(nc)::value;
+        const int ii = w + NW * n;
+        if (!FP8 && n == C::kPerWave - 1 && ii >= C::kInst) return;
+        // (Operands bound to locals: with the expressions inline in the
+        // builtin's argument list the host pass drops this kernel's stub.)
+        const char* src = base + cp_off[n];
+        DCP_LDS char* ldst = ii < C::kInst ? ring + (j % kStages) * C::kStageB + ii * 1024 : pad;
+        __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, 0);
+      };
+
       // Copy tile j of this window into ring stage j % kStages. Every wave
-      // issues exactly C::kOps vector-memory operations per tile.
+      // issues its fixed number of vector-memory operations per tile.
       auto issue = [&](int j) {
         const int tau0 = j * kT;
         DCP_LDS char* dst = ring + (j % kStages) * C::kStageB;
         if constexpr (BS32) {
-          // One block for the whole tile; an unusable id reads block 0 instead
-          // (the rows are zeroed after landing).
-          const int id = wave_uniform(ids[tau0 / bs]);
-          const char* base = a.kv;
-          if (id >= 0 && id < a.ncb)
-            base += static_cast<long long>(id) * a.block_stride_b +
-                    static_cast<long long>(tau0 % bs) * a.token_stride_b;
-#pragma unroll
-          for (int n = 0; n < C::kPerWave; ++n) {
-            const int ii = w + NW * n;
-            // (Operands bound to locals: with the expressions inline in the
-            // builtin's argument list the host pass drops this kernel's stub.)
-            const char* src = base + cp_off[n];
-            DCP_LDS char* ldst = ii < C::kInst ? dst + ii * 1024 : pad;
-            __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, 0);
-          }
+          const char* base = tile_src(j);
+          static_for<0, C::kPerWave>([&](auto nc) { copy_one(nc, base, j); });
         } else {
 #pragma unroll
           for (int n = 0; n < C::kPerWave; ++n) {
             const int ii = w + NW * n;
+            if (!FP8 && ii >= C::kInst) continue;
             const char* src = a.kv;
             DCP_LDS char* ldst = pad;
             if (ii < C::kInst) {
@@ -446,7 +496,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
       unsigned long long vm_next = 0;
       if constexpr (FP8) {
         // Widen tile 0 before the loop; tile k + 1 is widened while tile k is consumed.
-        wait_tiles_after<C>(min(kStages - 2, ntiles - 1));
+        wait_tiles(min(kStages - 2, ntiles - 1));
         lds_barrier();
         widen(0, valid_rows(0));
         if (ntiles > 1) vm_next = valid_rows(1);
@@ -455,8 +505,14 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
       for (int k = 0; k < ntiles; ++k) {
         uint32_t tile;
         unsigned long long vm_k;
+        // bf16 with whole-tile blocks: the copies of tile k + kStages - 1 are
+        // spread over the score MFMAs below instead of issued in one burst, so
+        // the waves do not all stall on a full memory queue at the same time.
+        constexpr bool kSpread = BS32 && !FP8;
+        const bool do_issue = k + kStages - 1 < ntiles;
+        const char* nsrc = nullptr;
         if constexpr (!FP8) {
-          wait_tiles_after<C>(min(kStages - 2, ntiles - 1 - k));
+          wait_tiles(min(kStages - 2, ntiles - 1 - k));
           vm_k = valid_rows(k);
           if (vm_k != 0xffffffffull) {
             // Zero the rows that were filled from the safe address, once every
@@ -468,17 +524,21 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
                 *reinterpret_cast<DCP_LDS i32x4*>(st + 16 * u) = i32x4{0, 0, 0, 0};
           }
           lds_barrier();
-          if (k + kStages - 1 < ntiles) issue(k + kStages - 1);
+          if constexpr (kSpread) {
+            if (do_issue) nsrc = tile_src(k + kStages - 1);
+          } else {
+            if (do_issue) issue(k + kStages - 1);
+          }
           tile = ring_addr + (k % kStages) * kTileB;
         } else {
           // Tile k is already widened (previous iteration or prologue).
           vm_k = k == 0 ? valid_rows(0) : vm_next;
           if (k + 1 < ntiles) {
-            wait_tiles_after<C>(min(1, ntiles - 2 - k));
+            wait_tiles(min(1, ntiles - 2 - k));
             vm_next = valid_rows(k + 1);
           }
           lds_barrier();
-          if (k + kStages - 1 < ntiles) issue(k + kStages - 1);
+          if (do_issue) issue(k + kStages - 1);
           if (k + 1 < ntiles) widen(k + 1, vm_next);
           tile = aux_addr + C::kF16Off + (k & 1) * kTileB;
         }
@@ -502,6 +562,13 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
           wait_lgkm<ahead>(ra[kk % kSRing]);
           if constexpr (kk & 1) sb = E::mfma(ra[kk % kSRing], qf[kk], sb);
           else sa = E::mfma(ra[kk % kSRing], qf[kk], sa);
+          if constexpr (kSpread) {
+            // copies n in [n0, n1) go out after this K step
+            constexpr int n0 = kk * C::kPerWave / kKSteps;
+            constexpr int n1 = (kk + 1) * C::kPerWave / kKSteps;
+            if (do_issue)
+              static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, k + kStages - 1); });
+          }
         });
         const f32x4 sv = sa + sb;
 
@@ -523,54 +590,82 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
           x[i] = ((vm_k >> r) & 1ull) ? sv[i] * sig[i] * a.scale_log2 : -INFINITY;
         }
         float hmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        hmax = fmaxf(hmax, __shfl_xor(hmax, 16));
-        hmax = fmaxf(hmax, __shfl_xor(hmax, 32));
-        if (q4 == 0) mx[(th * 16 + l16) * 4 + hg] = hmax;
-        lds_barrier();
-
-        // ---- part 2: every wave updates the reference max of heads 16nt + l16
-        float alpha[HG];
-        bool any_raise = false;
-        {
-          const f32x4 m0 = *reinterpret_cast<const DCP_LDS f32x4*>(mx + l16 * 4);
-          const f32x4 m1 = *reinterpret_cast<const DCP_LDS f32x4*>(mx + (16 + l16) * 4);
-#pragma unroll
-          for (int nt = 0; nt < HG; ++nt) {
-            const float tmax = fmaxf(m0[nt], m1[nt]);
-            // bf16 cache: probabilities may reach 2^8 before a rescale. fp8
-            // cache: rescale on any increase, so p <= 1 and p * scale stays
-            // inside the fp16 range.
-            const bool raise = tmax > m_ref[nt] + (FP8 ? 0.f : 8.f);
-            alpha[nt] = raise ? fast_exp2(m_ref[nt] - tmax) : 1.f;  // 0 when m_ref = -inf
-            m_ref[nt] = raise ? tmax : m_ref[nt];
-            any_raise |= raise;
-          }
-        }
-        float m_own = m_ref[0], a_own = alpha[0];
-#pragma unroll
-        for (int nt = 1; nt < HG; ++nt)
-          if (nt == hg) { m_own = m_ref[nt]; a_own = alpha[nt]; }
-        const float m_use = m_own == -INFINITY ? 0.f : m_own;
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m_use);
-        l_run = l_run * a_own + ((p[0] + p[1]) + (p[2] + p[3]));
+        hmax = max_xor32(max_xor16(hmax));
         // P^T fragment half of this wave: tokens 16th + 4q4 + i of head h_s.
-        {
-          const uint32_t lo = E::pack2(FP8 ? p[0] * sig[0] : p[0], FP8 ? p[1] * sig[1] : p[1]);
-          const uint32_t hi = E::pack2(FP8 ? p[2] * sig[2] : p[2], FP8 ? p[3] * sig[3] : p[3]);
+        auto store_p = [&](const float* pv) {
+          const uint32_t lo = E::pack2(FP8 ? pv[0] * sig[0] : pv[0], FP8 ? pv[1] * sig[1] : pv[1]);
+          const uint32_t hi = E::pack2(FP8 ? pv[2] * sig[2] : pv[2], FP8 ? pv[3] * sig[3] : pv[3]);
           *reinterpret_cast<DCP_LDS i32x2*>(aux + C::kPOff + ((hg * 64 + lane) * 2 + th) * 8) =
               i32x2{static_cast<int>(lo), static_cast<int>(hi)};
+        };
+        // bf16 cache: probabilities may reach 2^8 before the reference max of a
+        // head is raised. fp8 cache: it is raised on any increase, so p <= 1
+        // and p * scale stays inside the fp16 range.
+        constexpr float kRaise = FP8 ? 0.f : 8.f;
+        float p[4];
+        bool slow = true;
+        if constexpr (!FP8) {
+          // Fast path: probabilities against the current reference max, and one
+          // vote per wave on whether any head of its group needs a raise. Only
+          // when some wave votes yes do the waves exchange their maxima.
+          float m_own = m_ref[0];
+#pragma unroll
+          for (int nt = 1; nt < HG; ++nt)
+            if (nt == hg) m_own = m_ref[nt];
+          const float m_use = m_own == -INFINITY ? 0.f : m_own;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m_use);
+          store_p(p);
+          const bool need = __ballot(hmax > m_own + kRaise) != 0ull;
+          // (The vote is written and read with explicit-wait asm: as plain LDS
+          // accesses the compiler waits for every in-flight copy first.)
+          if (lane == 0) lds_store_b8(flags_addr + w, need ? 1 : 0);
+          lds_barrier();
+          i32x2 votes;
+          lds_b64<0>(votes, flags_addr);
+          wait_lgkm<0>(votes);
+          slow = wave_uniform((votes[0] | votes[1]) != 0);
+          if (!slow) l_run += (p[0] + p[1]) + (p[2] + p[3]);
         }
-        lds_barrier();
+        if (slow) {  // some wave votes for a raise (always, for fp8)
+          if (q4 == 0) mx[(th * 16 + l16) * 4 + hg] = hmax;
+          lds_barrier();
+
+          // Exchange the halves' maxima; every wave then raises the reference
+          // max of heads 16nt + l16 where needed, identically in every wave.
+          float alpha[HG];
+          bool any_raise = false;
+          {
+            const f32x4 m0 = *reinterpret_cast<const DCP_LDS f32x4*>(mx + l16 * 4);
+            const f32x4 m1 = *reinterpret_cast<const DCP_LDS f32x4*>(mx + (16 + l16) * 4);
+#pragma unroll
+            for (int nt = 0; nt < HG; ++nt) {
+              const float tmax = fmaxf(m0[nt], m1[nt]);
+              const bool raise = tmax > m_ref[nt] + kRaise;
+              alpha[nt] = raise ? fast_exp2(m_ref[nt] - tmax) : 1.f;  // 0 when m_ref = -inf
+              m_ref[nt] = raise ? tmax : m_ref[nt];
+              any_raise |= raise;
+            }
+          }
+          float m_own = m_ref[0], a_own = alpha[0];
+#pragma unroll
+          for (int nt = 1; nt < HG; ++nt)
+            if (nt == hg) { m_own = m_ref[nt]; a_own = alpha[nt]; }
+          const float m_use = m_own == -INFINITY ? 0.f : m_own;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m_use);
+          l_run = l_run * a_own + ((p[0] + p[1]) + (p[2] + p[3]));
+          store_p(p);
+          lds_barrier();
+          if (__ballot(any_raise)) {
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+              for (int nt = 0; nt < HG; ++nt) acc[mt][nt] *= alpha[nt];
+          }
+        }
 
         // ---- O^T += C_tile^T . P^T over this wave's value slice, all head groups
-        if (__ballot(any_raise)) {
-#pragma unroll
-          for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < HG; ++nt) acc[mt][nt] *= alpha[nt];
-        }
         i32x4 pb[HG];
         const uint32_t pbase = aux_addr + C::kPOff + lane * 16;
         static_for<0, HG>([&](auto nc) {
@@ -606,8 +701,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
     }
 
     // ---- finalise the piece: normalise and store (O, LSE) in slot s + g
-    float l_h = l_run + __shfl_xor(l_run, 16);
-    l_h += __shfl_xor(l_h, 32);
+    const float l_h = sum_xor32(sum_xor16(l_run));
     if (q4 == 0) lsum[th * 64 + 16 * hg + l16] = l_h;
     __syncthreads();
     const size_t slot = static_cast<size_t>(s) + g;

@@ -719,6 +719,375 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 cache, 64 heads per work group, blocks holding a multiple of 32 tokens:
+// producer / consumer form with one barrier per tile.
+//  * Waves 0-3 ("score waves") own 16 heads each. For tile s they compute S^T
+//    over all 32 tokens, run the online softmax of their own heads (so no
+//    maxima cross waves) and write P^T and any rescale factors to LDS.
+//  * Waves 4-7 ("value waves") own 128 value columns each, for all 64 heads,
+//    and accumulate O^T += C^T . P^T for tile s - 1 in the same step.
+//  * Waves w and w + 4 share a SIMD, so one wave's softmax, LDS waits and
+//    copy issue overlap the other's MFMAs.
+//  * The copy ring holds tile s (scores), tile s - 1 (values) and the two
+//    tiles after s in flight; the copies of tile s + 2 go out during step s,
+//    spread over both kinds of waves' MFMA loops.
+struct PP {
+  static constexpr int kMT = 8;                           // 16-column M tiles per value wave
+  static constexpr int kPerWave = (kDmaInst + 7) / 8;     // copies per wave and tile (at most)
+  static constexpr int kHiWaves = kDmaInst % 8 ? kDmaInst % 8 : 8;  // copy groups with kPerWave
+  static constexpr int kSDist = 3;                        // score K steps of fragments read ahead
+  static constexpr int kSRing = kSDist + 2;
+  static constexpr int kPD = 4;                           // value M tiles of reads in flight
+  static constexpr int kRingB = kStages * kTileB;
+  static constexpr int kPBufB = 4 * 64 * 16;              // P^T of one tile, 4 head groups
+  static constexpr int kPOff = 0;                         // [2] tiles
+  static constexpr int kAlphaOff = kPOff + 2 * kPBufB;    // [2][16 lanes][4 groups] floats
+  static constexpr int kFlagOff = kAlphaOff + 2 * 64 * 4; // [2][4] bytes
+  static constexpr int kFinOff = kFlagOff + 16;           // [64] head sums
+  static constexpr int kIdsOff = kFinOff + 64 * 4;
+  static constexpr int kAuxB = kIdsOff + kIdWin * 4;
+  static_assert(kRingB + kAuxB <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ void lds_store_b32(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_store_b128(uint32_t addr, i32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void lds_b32(int& r, uint32_t addr) {
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+}
+
+__global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
+  using E = Elt<false>;
+  __shared__ __attribute__((aligned(16))) char ring_raw[PP::kRingB];
+  __shared__ __attribute__((aligned(16))) char aux_raw[PP::kAuxB];
+  DCP_LDS char* ring = (DCP_LDS char*)ring_raw;
+  DCP_LDS char* aux = (DCP_LDS char*)aux_raw;
+  DCP_LDS int* ids = (DCP_LDS int*)(aux + PP::kIdsOff);
+  DCP_LDS float* fin = (DCP_LDS float*)(aux + PP::kFinOff);
+  const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+  const uint32_t aux_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aux));
+
+  const int lane = threadIdx.x & 63;
+  const int w = wave_uniform(threadIdx.x >> 6);
+  const bool scorer = w < 4;
+  const int grp = w & 3;  // score waves: head group; value waves: value slice
+  const int q4 = lane >> 4;
+  const int l16 = lane & 15;
+  const int g = xcd_logical_group(blockIdx.x, kGroups);
+  const int head0 = blockIdx.y * 64;
+  const int chunk = a.hdr->chunk;
+  const int total = a.hdr->total;
+  int pos = g * chunk;
+  const int end = min(pos + chunk, total);
+  if (pos >= end) return;
+  int s = find_segment(a.seg_off, a.S, pos);
+  const int bs = a.map.bs;
+
+  // Copies: copy group cw issues slots cw + 8n of a tile. The value waves take
+  // the groups with the extra copy (their MFMA loop has more room for them).
+  const int cw = (w + 4) & 7;
+  const bool hi_wave = cw < PP::kHiWaves;
+  int32_t cp_off[PP::kPerWave];
+#pragma unroll
+  for (int n = 0; n < PP::kPerWave; ++n) {
+    const int ii = cw + 8 * n;
+    int row = 0, c = 0;
+    if (ii < kDmaInst) slot_row_chunk<false>(ii * 64 + lane, row, c);
+    cp_off[n] = static_cast<int32_t>(row * a.token_stride_b) + 16 * c;
+  }
+  auto wait_tiles = [&](int n_after) {
+    if (hi_wave) wait_tiles_after_n<PP::kPerWave>(n_after);
+    else wait_tiles_after_n<PP::kPerWave - 1>(n_after);
+  };
+
+  // Score waves: A fragments of M tile 0 (row l16) and 1 (row 16 + l16),
+  // chunk 4kk + q4 (even kk) or 4 + 4(kk - 1) + q4 (odd kk).
+  const int r0 = l16, r1 = 16 + l16;
+  const uint32_t a0e = r0 * kRowB + 16 * (q4 ^ swz(r0));
+  const uint32_t a0o = r0 * kRowB + 16 * ((4 + q4) ^ swz(r0));
+  const uint32_t a1e = r1 * kRowB + 16 * (q4 ^ swz(r1));
+  const uint32_t a1o = r1 * kRowB + 16 * ((4 + q4) ^ swz(r1));
+  // Value waves: transposed A fragments, lane (k = l16 / 4, m = l16 % 4) at rows
+  // 4q4 + k and 16 + 4q4 + k, columns vbase + 16mt + 4m .. +3.
+  const int vbase = 128 * grp;
+  uint32_t t_off[8];
+  {
+    const int t_k = l16 >> 2, t_m = l16 & 3;
+    const int t_row0 = 4 * q4 + t_k, t_row1 = 16 + 4 * q4 + t_k;
+    const int cgrp = 128 * (vbase / 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 2 * j + (t_m >> 1);
+      t_off[j] = cgrp + t_row0 * kRowB + 16 * (c ^ swz(t_row0)) + 8 * (t_m & 1);
+      t_off[4 + j] = cgrp + t_row1 * kRowB + 16 * (c ^ swz(t_row1)) + 8 * (t_m & 1);
+    }
+  }
+  const uint32_t flags_addr = aux_addr + PP::kFlagOff;
+  if (threadIdx.x < 16) aux[PP::kFlagOff + threadIdx.x] = 0;
+
+  // The two roles run the same loops and barriers with separate code, so the
+  // register allocator sees the query fragments of one and the accumulators
+  // of the other as never live at the same time.
+  auto run = [&](auto role) {
+  constexpr bool kScorer = decltype(role)::value;
+  while (pos < end) {
+    while (a.seg_off[s + 1] <= pos) ++s;
+    const int seg_a = a.seg_off[s];
+    const int pe = min(end, a.seg_off[s + 1]);
+    const Piece p = make_piece(a.map, s, pos - seg_a, pe - seg_a);
+    const int32_t* trow = a.map.table + static_cast<size_t>(p.b) * a.map.width;
+
+    // Score waves: the 18 query fragments of head head0 + 16grp + l16 (B
+    // operand of S^T, columns 32kk + 8q4 .. +7). Value waves: O^T
+    // accumulators, M tile mt and head tile nt at 4mt + nt.
+    constexpr int kSt = kScorer ? kKSteps : 4 * PP::kMT;
+    f32x4 st[kSt];
+    if constexpr (kScorer) {
+      const uint16_t* qrow =
+          a.q + (static_cast<size_t>(p.b) * a.Hq + head0 + 16 * grp + l16) * kQK + 8 * q4;
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk)
+        st[kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + 32 * kk));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSt; ++i) st[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float m_ref = -INFINITY;  // score waves: reference max (log2 units) of head 16grp + l16
+    float l_run = 0.f;        // score waves: this lane's probability sum for that head
+
+    for (int wb = p.i0; wb < p.i1; wb += kIdWin) {
+      const int we = min(p.i1, wb + kIdWin);
+      const int ntok = (we - wb) * bs - (we == p.i1 ? (p.i1 - p.i0) * bs - p.ntok : 0);
+      for (int i = threadIdx.x; i < we - wb; i += 512) ids[i] = trow[p.r + a.map.D * (wb + i)];
+      wait_vm<0>();
+      __syncthreads();
+      const int ntiles = (ntok + kT - 1) / kT;
+
+      auto tile_src = [&](int j) -> const char* {
+        const int tau0 = j * kT;
+        const int id = wave_uniform(ids[tau0 / bs]);
+        const char* base = a.kv;
+        if (id >= 0 && id < a.ncb)
+          base += static_cast<long long>(id) * a.block_stride_b +
+                  static_cast<long long>(tau0 % bs) * a.token_stride_b;
+        return base;
+      };
+      auto copy_one = [&](auto nc, const char* base, int j) {
+        constexpr int n = decltype(nc)::value;
+        const int ii = cw + 8 * n;
+        if (n == PP::kPerWave - 1 && ii >= kDmaInst) return;
+        // (Operands bound to locals: with the expressions inline in the
+        // builtin's argument list the host pass drops this kernel's stub.)
+        const char* src = base + cp_off[n];
+        DCP_LDS char* ldst = ring + (j % kStages) * kTileB + ii * 1024;
+        __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, 0);
+      };
+      for (int j = 0; j < 2 && j < ntiles; ++j) {
+        const char* base = tile_src(j);
+        static_for<0, PP::kPerWave>([&](auto nc) { copy_one(nc, base, j); });
+      }
+
+      // Start of step ks (score waves on tile ks, value waves on tile ks - 1):
+      // this wave's copies of tile ks have landed, then the barrier makes every
+      // wave's copies visible and guarantees that step ks - 1 is finished, so
+      // the stage of tile ks - 2 is free for tile ks + 2. Returns the mask of
+      // tile ks's rows that hold real tokens of usable blocks. Both roles pass
+      // the same barriers in the same order.
+      auto step_begin = [&](int ks) -> unsigned long long {
+        if (ks < ntiles) wait_tiles(ks + 1 < ntiles ? 1 : 0);
+        lds_barrier();
+        unsigned long long vm = 0;
+        if (ks < ntiles) {
+          const int id = ids[ks * kT / bs];
+          const int n = min(kT, ntok - ks * kT);
+          vm = (id >= 0 && id < a.ncb) ? ((1ull << n) - 1) : 0ull;
+          if (vm != 0xffffffffull) {
+            // Rows past the end (or of an unusable block) were read from a safe
+            // address; zero them before any wave reads the tile.
+            DCP_LDS char* stg = ring + (ks % kStages) * kTileB;
+            for (int u = threadIdx.x; u < kTileCh; u += 512)
+              if (!((vm >> (u / kRowCh)) & 1ull))
+                *reinterpret_cast<DCP_LDS i32x4*>(stg + 16 * u) = i32x4{0, 0, 0, 0};
+            lds_barrier();
+          }
+        }
+        return vm;
+      };
+
+      if constexpr (kScorer) {
+        for (int ks = 0; ks < ntiles; ++ks) {
+          const unsigned long long vm = step_begin(ks);
+          const bool do_issue = ks + 2 < ntiles;
+          const char* nsrc = do_issue ? tile_src(ks + 2) : nullptr;
+          const uint32_t tile = ring_addr + (ks % kStages) * kTileB;
+          i32x4 ra[PP::kSRing], rb[PP::kSRing];
+          auto s_issue = [&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            constexpr int off = 128 * (kk >> 1);
+            if constexpr (kk & 1) {
+              lds_b128<off>(ra[kk % PP::kSRing], tile + a0o);
+              lds_b128<off>(rb[kk % PP::kSRing], tile + a1o);
+            } else {
+              lds_b128<off>(ra[kk % PP::kSRing], tile + a0e);
+              lds_b128<off>(rb[kk % PP::kSRing], tile + a1e);
+            }
+          };
+          static_for<0, PP::kSDist>(s_issue);
+          f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
+          static_for<0, kKSteps>([&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            if constexpr (kk + PP::kSDist < kKSteps) s_issue(IC<kk + PP::kSDist>{});
+            constexpr int ahead = kk + PP::kSDist < kKSteps ? PP::kSDist : kKSteps - 1 - kk;
+            wait_lgkm<2 * ahead>(ra[kk % PP::kSRing], rb[kk % PP::kSRing]);
+            const bf16x8 qv = __builtin_bit_cast(bf16x8, st[kk]);
+            if constexpr (kk & 1) {
+              s0b = E::mfma(ra[kk % PP::kSRing], qv, s0b);
+              s1b = E::mfma(rb[kk % PP::kSRing], qv, s1b);
+            } else {
+              s0a = E::mfma(ra[kk % PP::kSRing], qv, s0a);
+              s1a = E::mfma(rb[kk % PP::kSRing], qv, s1a);
+            }
+            // copies n in [n0, n1) go out after this K step
+            constexpr int n0 = kk * PP::kPerWave / kKSteps;
+            constexpr int n1 = (kk + 1) * PP::kPerWave / kKSteps;
+            if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + 2); });
+          });
+          const f32x4 sv0 = s0a + s0b, sv1 = s1a + s1b;
+
+          // Online softmax of head 16grp + l16 over this lane's 8 tokens
+          // (4q4 + i and 16 + 4q4 + i), exp2 domain.
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[i] = ((vm >> (4 * q4 + i)) & 1ull) ? sv0[i] * a.scale_log2 : -INFINITY;
+            x[4 + i] = ((vm >> (16 + 4 * q4 + i)) & 1ull) ? sv1[i] * a.scale_log2 : -INFINITY;
+          }
+          float hmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+          hmax = max_xor32(max_xor16(hmax));
+          // The reference only rises when the tile's max exceeds it by more
+          // than 8, so probabilities stay <= 256 and rescales are rare.
+          const bool raise = hmax > m_ref + 8.f;
+          const float alpha = raise ? fast_exp2(m_ref - hmax) : 1.f;  // 0 when m_ref = -inf
+          m_ref = raise ? hmax : m_ref;
+          const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+          float pr[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(x[i] - m_use);
+          l_run = l_run * alpha +
+                  (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+          const i32x4 pk = {static_cast<int>(E::pack2(pr[0], pr[1])),
+                            static_cast<int>(E::pack2(pr[2], pr[3])),
+                            static_cast<int>(E::pack2(pr[4], pr[5])),
+                            static_cast<int>(E::pack2(pr[6], pr[7]))};
+          lds_store_b128(aux_addr + PP::kPOff + (ks & 1) * PP::kPBufB + (grp * 64 + lane) * 16, pk);
+          const bool any = __ballot(raise) != 0ull;
+          if (lane == 0) lds_store_b8(flags_addr + (ks & 1) * 4 + grp, any ? 1 : 0);
+          if (any && q4 == 0)
+            lds_store_b32(aux_addr + PP::kAlphaOff + (((ks & 1) * 16 + l16) * 4 + grp) * 4, alpha);
+        }
+        step_begin(ntiles);  // the value waves' last step
+      } else {
+        // Step 0 has no value tile yet: only this wave's copies of tile 2.
+        step_begin(0);
+        if (2 < ntiles) {
+          const char* nsrc = tile_src(2);
+          static_for<0, PP::kPerWave>([&](auto nc) { copy_one(nc, nsrc, 2); });
+        }
+        for (int ks = 1; ks <= ntiles; ++ks) {
+          step_begin(ks);
+          const bool do_issue = ks + 2 < ntiles;
+          const char* nsrc = do_issue ? tile_src(ks + 2) : nullptr;
+          const int kv = ks - 1;
+          // Rescale factors of heads whose reference max rose in tile kv.
+          int fl;
+          lds_b32<0>(fl, flags_addr + (kv & 1) * 4);
+          wait_lgkm<0>(fl);
+          if (wave_uniform(fl) != 0) {
+            i32x4 al;
+            lds_b128<0>(al, aux_addr + PP::kAlphaOff + ((kv & 1) * 16 + l16) * 16);
+            wait_lgkm<0>(al);
+            const f32x4 alv = __builtin_bit_cast(f32x4, al);
+            const int fb = wave_uniform(fl);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+              if ((fb >> (8 * nt)) & 0xff)
+#pragma unroll
+                for (int mt = 0; mt < PP::kMT; ++mt) st[4 * mt + nt] *= alv[nt];
+          }
+          i32x4 pb[4];
+          const uint32_t pbase = aux_addr + PP::kPOff + (kv & 1) * PP::kPBufB + lane * 16;
+          static_for<0, 4>([&](auto nc) {
+            constexpr int nt = decltype(nc)::value;
+            lds_b128<nt * 1024>(pb[nt], pbase);
+          });
+          const uint32_t tile = ring_addr + (kv % kStages) * kTileB;
+          uint32_t tb[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) tb[j] = tile + t_off[j];
+          i32x2 rlo[PP::kPD + 2], rhi[PP::kPD + 2];
+          auto p_issue = [&](auto mc) {
+            constexpr int mt = decltype(mc)::value;
+            constexpr int off = 128 * (mt >> 2);
+            lds_tr<off>(rlo[mt % (PP::kPD + 2)], tb[mt & 3]);
+            lds_tr<off>(rhi[mt % (PP::kPD + 2)], tb[4 + (mt & 3)]);
+          };
+          static_for<0, PP::kPD>(p_issue);
+          static_for<0, PP::kMT>([&](auto mc) {
+            constexpr int mt = decltype(mc)::value;
+            if constexpr (mt + PP::kPD < PP::kMT) p_issue(IC<mt + PP::kPD>{});
+            constexpr int ahead = mt + PP::kPD < PP::kMT ? PP::kPD : PP::kMT - 1 - mt;
+            wait_lgkm<2 * ahead>(rlo[mt % (PP::kPD + 2)], rhi[mt % (PP::kPD + 2)]);
+            const i32x4 av = {rlo[mt % (PP::kPD + 2)][0], rlo[mt % (PP::kPD + 2)][1],
+                              rhi[mt % (PP::kPD + 2)][0], rhi[mt % (PP::kPD + 2)][1]};
+            static_for<0, 4>([&](auto nc) {
+              constexpr int nt = decltype(nc)::value;
+              st[4 * mt + nt] = E::mfma(av, __builtin_bit_cast(bf16x8, pb[nt]), st[4 * mt + nt]);
+            });
+            constexpr int n0 = mt * PP::kPerWave / PP::kMT;
+            constexpr int n1 = (mt + 1) * PP::kPerWave / PP::kMT;
+            if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + 2); });
+          });
+        }
+      }
+      __syncthreads();  // ring stages and ids are reused by the next window / piece
+    }
+
+    // ---- finalise the piece: normalise and store (O, LSE) in slot s + g
+    const size_t slot = static_cast<size_t>(s) + g;
+    if constexpr (kScorer) {
+      const float l_h = sum_xor32(sum_xor16(l_run));
+      if (q4 == 0) {
+        fin[16 * grp + l16] = l_h;
+        a.ws_lse[slot * a.Hq + head0 + 16 * grp + l16] =
+            l_h > 0.f ? (m_ref + fast_log2(l_h)) * kLn2 : -INFINITY;
+      }
+    }
+    __syncthreads();
+    if constexpr (!kScorer) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float l_tot = fin[16 * nt + l16];
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
+#pragma unroll
+        for (int mt = 0; mt < PP::kMT; ++mt)
+          *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
+      }
+    }
+    __syncthreads();  // fin is rewritten by the next piece
+    pos = pe;
+  }
+  };
+  if (scorer) run(IC<true>{});
+  else run(IC<false>{});
+}
+
 }  // namespace
 
 int mla_groups() { return kGroups; }
@@ -763,6 +1132,10 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   const bool bs32 = d->block_size % kT == 0 && a.token_stride_b * kT < (1ll << 30);
   const int heads = d->num_q_heads < 64 ? d->num_q_heads : 64;
   const dim3 grid(kGroups, d->num_q_heads / heads);
+  if (!fp8 && bs32 && heads == 64) {
+    hipLaunchKernelGGL(mla_pp_kernel, grid, dim3(512), 0, stream, a);
+    return hipGetLastError();
+  }
   switch (heads / 16) {
     case 1:
       if (fp8) launch_mla_hg<1, true>(a, bs32, grid, stream);

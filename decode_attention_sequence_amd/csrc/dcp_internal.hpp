@@ -42,6 +42,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct PlanHeader {
   int32_t chunk;  // blocks per work group (>= 1)
   int32_t total;  // blocks over all segments
+  int32_t pad[2];
+  int32_t zero[4];  // 16 zero bytes: copy source for tile rows without a token
 };
 // Workspace layout: PlanHeader, seg_off[S + 1] (int32), then at 256-byte
 // alignment lse slots [num_slots, Hq] fp32, then o slots [num_slots, Hq, v_dim] fp32.

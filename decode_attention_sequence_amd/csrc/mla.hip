@@ -87,6 +87,7 @@ struct MlaArgs {
   float* ws_lse;
   long long block_stride_b;  // bytes
   long long token_stride_b;  // bytes
+  const char* zero;         // 16 zero bytes (workspace)
   int S;
   int ncb;
   int Hq;
@@ -722,16 +723,21 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
 // ---------------------------------------------------------------------------
 // bf16 cache, 64 heads per work group, blocks holding a multiple of 32 tokens:
 // producer / consumer form with one barrier per tile.
-//  * Waves 0-3 ("score waves") own 16 heads each. For tile s they compute S^T
+//  * Waves 0-3 ("score waves") own 16 heads each. For tile t they compute S^T
 //    over all 32 tokens, run the online softmax of their own heads (so no
 //    maxima cross waves) and write P^T and any rescale factors to LDS.
 //  * Waves 4-7 ("value waves") own 128 value columns each, for all 64 heads,
-//    and accumulate O^T += C^T . P^T for tile s - 1 in the same step.
+//    and accumulate O^T += C^T . P^T for tile t - 1 in the same step.
 //  * Waves w and w + 4 share a SIMD, so one wave's softmax, LDS waits and
 //    copy issue overlap the other's MFMAs.
-//  * The copy ring holds tile s (scores), tile s - 1 (values) and the two
-//    tiles after s in flight; the copies of tile s + 2 go out during step s,
+//  * The copy ring holds tile t (scores), tile t - 1 (values) and the two
+//    tiles after t in flight; the copies of tile t + 2 go out during step t,
 //    spread over both kinds of waves' MFMA loops.
+//  * The tiles of a work group's whole range form one stream: a window of
+//    the range (up to kMaxTiles tiles of up to kMaxPieces segments) gets a
+//    tile table in LDS, and segment boundaries inside a window are handled
+//    per tile (state reset, query reload, result store) without draining the
+//    copy pipeline.
 struct PP {
   static constexpr int kMT = 8;                           // 16-column M tiles per value wave
   static constexpr int kPerWave = (kDmaInst + 7) / 8;     // copies per wave and tile (at most)
@@ -739,16 +745,25 @@ struct PP {
   static constexpr int kSDist = 3;                        // score K steps of fragments read ahead
   static constexpr int kSRing = kSDist + 2;
   static constexpr int kPD = 4;                           // value M tiles of reads in flight
+  static constexpr int kMaxPieces = 32;                   // segments per window
+  static constexpr int kMaxTiles = 640;                   // tiles per window
   static constexpr int kRingB = kStages * kTileB;
   static constexpr int kPBufB = 4 * 64 * 16;              // P^T of one tile, 4 head groups
   static constexpr int kPOff = 0;                         // [2] tiles
   static constexpr int kAlphaOff = kPOff + 2 * kPBufB;    // [2][16 lanes][4 groups] floats
   static constexpr int kFlagOff = kAlphaOff + 2 * 64 * 4; // [2][4] bytes
-  static constexpr int kFinOff = kFlagOff + 16;           // [64] head sums
-  static constexpr int kIdsOff = kFinOff + 64 * 4;
-  static constexpr int kAuxB = kIdsOff + kIdWin * 4;
+  static constexpr int kFinOff = kFlagOff + 16;           // [2][64] head sums
+  static constexpr int kPieceOff = kFinOff + 2 * 64 * 4;  // [kMaxPieces] x 2 int4
+  static constexpr int kTileOff = kPieceOff + kMaxPieces * 32;  // [kMaxTiles] int2
+  static constexpr int kMiscOff = kTileOff + kMaxTiles * 8;     // tiles, window end
+  static constexpr int kAuxB = kMiscOff + 16;
   static_assert(kRingB + kAuxB <= 160 * 1024, "LDS budget");
 };
+// Tile table entry: x = block id (-1: unusable, the tile reads the safe
+// address and is zeroed), y = tile offset in the block / 32 (bits 0-7),
+// valid rows - 1 (bits 8-15), piece (bits 16-23), first tile of its segment
+// (bit 30), last tile of its segment (bit 31).
+// Piece entry: {s, b, first local block, -}, {first tile, tiles, tokens, -}.
 
 __device__ __forceinline__ void lds_store_b32(uint32_t addr, float v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
@@ -767,8 +782,6 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) char aux_raw[PP::kAuxB];
   DCP_LDS char* ring = (DCP_LDS char*)ring_raw;
   DCP_LDS char* aux = (DCP_LDS char*)aux_raw;
-  DCP_LDS int* ids = (DCP_LDS int*)(aux + PP::kIdsOff);
-  DCP_LDS float* fin = (DCP_LDS float*)(aux + PP::kFinOff);
   const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
   const uint32_t aux_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aux));
 
@@ -780,25 +793,26 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   const int l16 = lane & 15;
   const int g = xcd_logical_group(blockIdx.x, kGroups);
   const int head0 = blockIdx.y * 64;
-  const int chunk = a.hdr->chunk;
   const int total = a.hdr->total;
-  int pos = g * chunk;
-  const int end = min(pos + chunk, total);
-  if (pos >= end) return;
-  int s = find_segment(a.seg_off, a.S, pos);
+  const int range0 = g * a.hdr->chunk;
+  const int end = min(range0 + a.hdr->chunk, total);
+  if (range0 >= end) return;
   const int bs = a.map.bs;
+  const int D = a.map.D;
 
   // Copies: copy group cw issues slots cw + 8n of a tile. The value waves take
   // the groups with the extra copy (their MFMA loop has more room for them).
   const int cw = (w + 4) & 7;
   const bool hi_wave = cw < PP::kHiWaves;
   int32_t cp_off[PP::kPerWave];
+  int cp_row[PP::kPerWave];  // tile row this lane's copy n fills
 #pragma unroll
   for (int n = 0; n < PP::kPerWave; ++n) {
     const int ii = cw + 8 * n;
     int row = 0, c = 0;
     if (ii < kDmaInst) slot_row_chunk<false>(ii * 64 + lane, row, c);
     cp_off[n] = static_cast<int32_t>(row * a.token_stride_b) + 16 * c;
+    cp_row[n] = row;
   }
   auto wait_tiles = [&](int n_after) {
     if (hi_wave) wait_tiles_after_n<PP::kPerWave>(n_after);
@@ -828,102 +842,196 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
     }
   }
   const uint32_t flags_addr = aux_addr + PP::kFlagOff;
-  if (threadIdx.x < 16) aux[PP::kFlagOff + threadIdx.x] = 0;
+  const uint32_t tiles_addr = aux_addr + PP::kTileOff;
+  const uint32_t piece_addr = aux_addr + PP::kPieceOff;
+
+  // Tile table entry t of the current window (wave-uniform).
+  struct TileInfo {
+    int id, y;
+    __device__ int nvalid() const { return ((y >> 8) & 0xff) + 1; }
+    __device__ int piece() const { return (y >> 16) & 0xff; }
+    __device__ bool first() const { return (y >> 30) & 1; }
+    __device__ bool last() const { return (y >> 31) & 1; }
+    __device__ unsigned long long rows() const {
+      return id >= 0 ? (nvalid() == 32 ? 0xffffffffull : (1ull << nvalid()) - 1) : 0ull;
+    }
+  };
+  auto tile_info = [&](int t) -> TileInfo {
+    i32x2 e;
+    lds_b64<0>(e, tiles_addr + 8 * t);
+    wait_lgkm<0>(e);
+    return TileInfo{wave_uniform(e[0]), wave_uniform(e[1])};
+  };
+  auto piece_s = [&](int p) -> int {  // segment of piece p
+    int v;
+    lds_b32<0>(v, piece_addr + 32 * p);
+    wait_lgkm<0>(v);
+    return wave_uniform(v);
+  };
+  auto piece_b = [&](int p) -> int {  // sequence of piece p
+    int v;
+    lds_b32<4>(v, piece_addr + 32 * p);
+    wait_lgkm<0>(v);
+    return wave_uniform(v);
+  };
+  // Copy source of a tile: its block's rows, and for rows that hold no real
+  // token of a usable block, 16 zero bytes of the workspace instead (so no
+  // tile ever needs zeroing in LDS).
+  struct Src {
+    const char* base;
+    int nvalid;  // rows taken from the block
+  };
+  auto tile_src = [&](const TileInfo& ti) -> Src {
+    if (ti.id < 0) return Src{a.kv, 0};
+    return Src{a.kv + static_cast<long long>(ti.id) * a.block_stride_b +
+                   static_cast<long long>(32 * (ti.y & 0xff)) * a.token_stride_b,
+               ti.nvalid()};
+  };
+  auto copy_one = [&](auto nc, const Src& sr, int t) {
+    constexpr int n = decltype(nc)::value;
+    const int ii = cw + 8 * n;
+    if (n == PP::kPerWave - 1 && ii >= kDmaInst) return;
+    // (Operands bound to locals: with the expressions inline in the
+    // builtin's argument list the host pass drops this kernel's stub.)
+    const char* src = cp_row[n] < sr.nvalid ? sr.base + cp_off[n] : a.zero;
+    DCP_LDS char* ldst = ring + (t % kStages) * kTileB + ii * 1024;
+    __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, 0);
+  };
 
   // The two roles run the same loops and barriers with separate code, so the
   // register allocator sees the query fragments of one and the accumulators
   // of the other as never live at the same time.
   auto run = [&](auto role) {
-  constexpr bool kScorer = decltype(role)::value;
-  while (pos < end) {
-    while (a.seg_off[s + 1] <= pos) ++s;
-    const int seg_a = a.seg_off[s];
-    const int pe = min(end, a.seg_off[s + 1]);
-    const Piece p = make_piece(a.map, s, pos - seg_a, pe - seg_a);
-    const int32_t* trow = a.map.table + static_cast<size_t>(p.b) * a.map.width;
-
-    // Score waves: the 18 query fragments of head head0 + 16grp + l16 (B
-    // operand of S^T, columns 32kk + 8q4 .. +7). Value waves: O^T
-    // accumulators, M tile mt and head tile nt at 4mt + nt.
+    constexpr bool kScorer = decltype(role)::value;
+    // Score waves: the 18 query fragments of head head0 + 16grp + l16 of
+    // sequence qb (B operand of S^T, columns 32kk + 8q4 .. +7). Value waves:
+    // O^T accumulators, M tile mt and head tile nt at 4mt + nt.
     constexpr int kSt = kScorer ? kKSteps : 4 * PP::kMT;
     f32x4 st[kSt];
-    if constexpr (kScorer) {
+#pragma unroll
+    for (int i = 0; i < kSt; ++i) st[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int qb = -1;
+    auto load_q = [&](int b) {
       const uint16_t* qrow =
-          a.q + (static_cast<size_t>(p.b) * a.Hq + head0 + 16 * grp + l16) * kQK + 8 * q4;
+          a.q + (static_cast<size_t>(b) * a.Hq + head0 + 16 * grp + l16) * kQK + 8 * q4;
 #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk)
         st[kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + 32 * kk));
-    } else {
+      // Consume the loads here, in order: the compiler then waits for exactly
+      // these loads (and what was issued before them), instead of placing a
+      // wait for every outstanding copy in front of each later use.
 #pragma unroll
-      for (int i = 0; i < kSt; ++i) st[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int kk = 0; kk < kKSteps; ++kk) asm volatile("" : "+v"(st[kk]));
+      qb = b;
+    };
     float m_ref = -INFINITY;  // score waves: reference max (log2 units) of head 16grp + l16
     float l_run = 0.f;        // score waves: this lane's probability sum for that head
+    int nfin = 0;             // segments finished so far (parity selects the fin buffer)
 
-    for (int wb = p.i0; wb < p.i1; wb += kIdWin) {
-      const int we = min(p.i1, wb + kIdWin);
-      const int ntok = (we - wb) * bs - (we == p.i1 ? (p.i1 - p.i0) * bs - p.ntok : 0);
-      for (int i = threadIdx.x; i < we - wb; i += 512) ids[i] = trow[p.r + a.map.D * (wb + i)];
+    int wpos = range0;
+    int s_cur = find_segment(a.seg_off, a.S, wpos);
+    while (wpos < end) {
+      // ---- window [wpos, wend): piece table (wave 0), then tile table (all)
+      if (w == 0) {
+        const int sl = s_cur + lane;
+        int lo = total, hi = total;
+        if (sl < a.S) {
+          lo = a.seg_off[sl];
+          hi = a.seg_off[sl + 1];
+        }
+        int wend = end;
+        if (s_cur + PP::kMaxPieces <= a.S)
+          wend = min(wend, __shfl(hi, PP::kMaxPieces - 1));  // start of segment s_cur + 32
+        wend = min(wend, wpos + PP::kMaxTiles / (bs / kT));
+        const int pstart = max(lo, wpos);
+        const int pend = min(hi, wend);
+        const int nblk = (lane < PP::kMaxPieces && sl < a.S) ? max(0, pend - pstart) : 0;
+        int ntok = 0, b = 0, i0 = 0;
+        if (nblk > 0) {
+          b = sl / D;
+          const int r = sl - b * D;
+          i0 = pstart - lo;
+          const int i1 = pend - lo;
+          const int tail = bs * (r + D * (i1 - 1) + 1) - seq_tokens(a.map, b);
+          ntok = nblk * bs - max(tail, 0);
+        }
+        const int ntiles = (ntok + kT - 1) / kT;
+        int ts = ntiles;  // inclusive prefix sum -> first tile
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int v = __shfl_up(ts, off);
+          if (lane >= off) ts += v;
+        }
+        const int T = __shfl(ts, 63);
+        ts -= ntiles;
+        const int flags = (pstart == max(lo, range0) ? 1 : 0) | (pend == min(hi, end) ? 2 : 0);
+        if (lane < PP::kMaxPieces) {
+          *reinterpret_cast<DCP_LDS i32x4*>(aux + PP::kPieceOff + 32 * lane) = i32x4{sl, b, i0, 0};
+          *reinterpret_cast<DCP_LDS i32x4*>(aux + PP::kPieceOff + 32 * lane + 16) =
+              i32x4{ts, ntiles, ntok, flags};
+        }
+        if (lane == 0) *reinterpret_cast<DCP_LDS i32x4*>(aux + PP::kMiscOff) = i32x4{T, wend, 0, 0};
+      }
+      __syncthreads();
+      const i32x4 misc = *reinterpret_cast<const DCP_LDS i32x4*>(aux + PP::kMiscOff);
+      const int T = misc[0];
+      const int wend = misc[1];
+      for (int t = threadIdx.x; t < T; t += 512) {
+        // piece p: last piece whose first tile is <= t (a piece without tiles
+        // shares its first tile with the next one, which is found instead)
+        int p = 0;
+        for (int step = PP::kMaxPieces / 2; step > 0; step >>= 1) {
+          const int ts = *reinterpret_cast<const DCP_LDS int*>(aux + PP::kPieceOff + 32 * (p + step) + 16);
+          if (ts <= t) p += step;
+        }
+        const i32x4 pa = *reinterpret_cast<const DCP_LDS i32x4*>(aux + PP::kPieceOff + 32 * p);
+        const i32x4 pb = *reinterpret_cast<const DCP_LDS i32x4*>(aux + PP::kPieceOff + 32 * p + 16);
+        const int j = t - pb[0];
+        const int tok = j * kT;
+        const int b = pa[1];
+        const int col = (pa[0] - b * D) + D * (pa[2] + tok / bs);
+        int id = a.map.table[static_cast<size_t>(b) * a.map.width + col];
+        if (!(id >= 0 && id < a.ncb)) id = -1;
+        const int nvalid = min(kT, pb[2] - tok);
+        const unsigned y = static_cast<unsigned>((tok % bs) / kT) | (static_cast<unsigned>(nvalid - 1) << 8) |
+                           (static_cast<unsigned>(p) << 16) |
+                           ((j == 0 && (pb[3] & 1)) ? (1u << 30) : 0u) |
+                           ((j == pb[1] - 1 && (pb[3] & 2)) ? (1u << 31) : 0u);
+        *reinterpret_cast<DCP_LDS i32x2*>(aux + PP::kTileOff + 8 * t) = i32x2{id, static_cast<int>(y)};
+      }
       wait_vm<0>();
       __syncthreads();
-      const int ntiles = (ntok + kT - 1) / kT;
-
-      auto tile_src = [&](int j) -> const char* {
-        const int tau0 = j * kT;
-        const int id = wave_uniform(ids[tau0 / bs]);
-        const char* base = a.kv;
-        if (id >= 0 && id < a.ncb)
-          base += static_cast<long long>(id) * a.block_stride_b +
-                  static_cast<long long>(tau0 % bs) * a.token_stride_b;
-        return base;
-      };
-      auto copy_one = [&](auto nc, const char* base, int j) {
-        constexpr int n = decltype(nc)::value;
-        const int ii = cw + 8 * n;
-        if (n == PP::kPerWave - 1 && ii >= kDmaInst) return;
-        // (Operands bound to locals: with the expressions inline in the
-        // builtin's argument list the host pass drops this kernel's stub.)
-        const char* src = base + cp_off[n];
-        DCP_LDS char* ldst = ring + (j % kStages) * kTileB + ii * 1024;
-        __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, 0);
-      };
-      for (int j = 0; j < 2 && j < ntiles; ++j) {
-        const char* base = tile_src(j);
-        static_for<0, PP::kPerWave>([&](auto nc) { copy_one(nc, base, j); });
+      // prologue: tiles 0 and 1
+      for (int t = 0; t < 2 && t < T; ++t) {
+        const Src sr = tile_src(tile_info(t));
+        static_for<0, PP::kPerWave>([&](auto nc) { copy_one(nc, sr, t); });
       }
 
       // Start of step ks (score waves on tile ks, value waves on tile ks - 1):
       // this wave's copies of tile ks have landed, then the barrier makes every
       // wave's copies visible and guarantees that step ks - 1 is finished, so
-      // the stage of tile ks - 2 is free for tile ks + 2. Returns the mask of
-      // tile ks's rows that hold real tokens of usable blocks. Both roles pass
-      // the same barriers in the same order.
-      auto step_begin = [&](int ks) -> unsigned long long {
-        if (ks < ntiles) wait_tiles(ks + 1 < ntiles ? 1 : 0);
+      // the stage of tile ks - 2 is free for tile ks + 2. Both roles pass the
+      // same barriers in the same order.
+      auto step_begin = [&](int ks) {
+        if (ks < T) wait_tiles(ks + 1 < T ? 1 : 0);
         lds_barrier();
-        unsigned long long vm = 0;
-        if (ks < ntiles) {
-          const int id = ids[ks * kT / bs];
-          const int n = min(kT, ntok - ks * kT);
-          vm = (id >= 0 && id < a.ncb) ? ((1ull << n) - 1) : 0ull;
-          if (vm != 0xffffffffull) {
-            // Rows past the end (or of an unusable block) were read from a safe
-            // address; zero them before any wave reads the tile.
-            DCP_LDS char* stg = ring + (ks % kStages) * kTileB;
-            for (int u = threadIdx.x; u < kTileCh; u += 512)
-              if (!((vm >> (u / kRowCh)) & 1ull))
-                *reinterpret_cast<DCP_LDS i32x4*>(stg + 16 * u) = i32x4{0, 0, 0, 0};
-            lds_barrier();
-          }
-        }
-        return vm;
       };
 
       if constexpr (kScorer) {
-        for (int ks = 0; ks < ntiles; ++ks) {
-          const unsigned long long vm = step_begin(ks);
-          const bool do_issue = ks + 2 < ntiles;
-          const char* nsrc = do_issue ? tile_src(ks + 2) : nullptr;
+        for (int ks = 0; ks < T; ++ks) {
+          step_begin(ks);
+          const TileInfo ti = tile_info(ks);
+          if (ti.first()) {
+            m_ref = -INFINITY;
+            l_run = 0.f;
+            // A new sequence needs its query. (Loaded here, in the iteration
+            // that uses it, the compiler's waits for it are exact and do not
+            // drain the copies in flight.)
+            const int b = piece_b(ti.piece());
+            if (b != qb) load_q(b);
+          }
+          const bool do_issue = ks + 2 < T;
+          const Src nsrc = do_issue ? tile_src(tile_info(ks + 2)) : Src{a.kv, 0};
           const uint32_t tile = ring_addr + (ks % kStages) * kTileB;
           i32x4 ra[PP::kSRing], rb[PP::kSRing];
           auto s_issue = [&](auto kc) {
@@ -961,6 +1069,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
 
           // Online softmax of head 16grp + l16 over this lane's 8 tokens
           // (4q4 + i and 16 + 4q4 + i), exp2 domain.
+          const unsigned long long vm = ti.rows();
           float x[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -990,30 +1099,41 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           if (lane == 0) lds_store_b8(flags_addr + (ks & 1) * 4 + grp, any ? 1 : 0);
           if (any && q4 == 0)
             lds_store_b32(aux_addr + PP::kAlphaOff + (((ks & 1) * 16 + l16) * 4 + grp) * 4, alpha);
+          if (ti.last()) {
+            // Segment done: its head sums for the value waves, and its LSE.
+            const float l_h = sum_xor32(sum_xor16(l_run));
+            if (q4 == 0) {
+              lds_store_b32(aux_addr + PP::kFinOff + ((nfin & 1) * 64 + 16 * grp + l16) * 4, l_h);
+              const size_t slot = static_cast<size_t>(piece_s(ti.piece())) + g;
+              a.ws_lse[slot * a.Hq + head0 + 16 * grp + l16] =
+                  l_h > 0.f ? (m_ref + fast_log2(l_h)) * kLn2 : -INFINITY;
+            }
+            ++nfin;
+          }
         }
-        step_begin(ntiles);  // the value waves' last step
+        step_begin(T);  // the value waves' last step
       } else {
         // Step 0 has no value tile yet: only this wave's copies of tile 2.
         step_begin(0);
-        if (2 < ntiles) {
-          const char* nsrc = tile_src(2);
+        if (2 < T) {
+          const Src nsrc = tile_src(tile_info(2));
           static_for<0, PP::kPerWave>([&](auto nc) { copy_one(nc, nsrc, 2); });
         }
-        for (int ks = 1; ks <= ntiles; ++ks) {
+        for (int ks = 1; ks <= T; ++ks) {
           step_begin(ks);
-          const bool do_issue = ks + 2 < ntiles;
-          const char* nsrc = do_issue ? tile_src(ks + 2) : nullptr;
+          const bool do_issue = ks + 2 < T;
+          const Src nsrc = do_issue ? tile_src(tile_info(ks + 2)) : Src{a.kv, 0};
           const int kv = ks - 1;
           // Rescale factors of heads whose reference max rose in tile kv.
           int fl;
           lds_b32<0>(fl, flags_addr + (kv & 1) * 4);
           wait_lgkm<0>(fl);
-          if (wave_uniform(fl) != 0) {
+          const int fb = wave_uniform(fl);
+          if (fb != 0) {
             i32x4 al;
             lds_b128<0>(al, aux_addr + PP::kAlphaOff + ((kv & 1) * 16 + l16) * 16);
             wait_lgkm<0>(al);
             const f32x4 alv = __builtin_bit_cast(f32x4, al);
-            const int fb = wave_uniform(fl);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
               if ((fb >> (8 * nt)) & 0xff)
@@ -1053,36 +1173,40 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             constexpr int n1 = (mt + 1) * PP::kPerWave / PP::kMT;
             if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + 2); });
           });
+          const TileInfo ti = tile_info(kv);
+          if (ti.last()) {
+            // Segment done: normalise by the score waves' head sums and store
+            // (O, slot s + g); the accumulators restart at zero.
+            const size_t slot = static_cast<size_t>(piece_s(ti.piece())) + g;
+            // fin[16nt + l16] for nt = 0..3
+            const uint32_t fa = aux_addr + PP::kFinOff + ((nfin & 1) * 64 + l16) * 4;
+            int l0, l1, l2, l3;
+            lds_b32<0>(l0, fa);
+            lds_b32<64>(l1, fa);
+            lds_b32<128>(l2, fa);
+            lds_b32<192>(l3, fa);
+            wait_lgkm<0>(l0, l1);
+            wait_lgkm<0>(l2, l3);
+            const float lt[4] = {__int_as_float(l0), __int_as_float(l1), __int_as_float(l2),
+                                 __int_as_float(l3)};
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+              const float inv = lt[nt] > 0.f ? 1.f / lt[nt] : 0.f;
+              float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
+#pragma unroll
+              for (int mt = 0; mt < PP::kMT; ++mt) {
+                *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
+                st[4 * mt + nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+              }
+            }
+            ++nfin;
+          }
         }
       }
-      __syncthreads();  // ring stages and ids are reused by the next window / piece
+      __syncthreads();  // ring stages and tables are reused by the next window
+      wpos = wend;
+      if (wpos < end) s_cur = find_segment(a.seg_off, a.S, wpos);
     }
-
-    // ---- finalise the piece: normalise and store (O, LSE) in slot s + g
-    const size_t slot = static_cast<size_t>(s) + g;
-    if constexpr (kScorer) {
-      const float l_h = sum_xor32(sum_xor16(l_run));
-      if (q4 == 0) {
-        fin[16 * grp + l16] = l_h;
-        a.ws_lse[slot * a.Hq + head0 + 16 * grp + l16] =
-            l_h > 0.f ? (m_ref + fast_log2(l_h)) * kLn2 : -INFINITY;
-      }
-    }
-    __syncthreads();
-    if constexpr (!kScorer) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float l_tot = fin[16 * nt + l16];
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
-#pragma unroll
-        for (int mt = 0; mt < PP::kMT; ++mt)
-          *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
-      }
-    }
-    __syncthreads();  // fin is rewritten by the next piece
-    pos = pe;
-  }
   };
   if (scorer) run(IC<true>{});
   else run(IC<false>{});
@@ -1119,6 +1243,7 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   a.seg_off = L.ws.seg_off;
   a.ws_o = L.ws.o;
   a.ws_lse = L.ws.lse;
+  a.zero = reinterpret_cast<const char*>(L.ws.header->zero);
   const int elt = d->kv_dtype == DCP_BF16 ? 2 : 1;
   a.block_stride_b = d->kv_block_stride * elt;
   a.token_stride_b = d->kv_token_stride * elt;

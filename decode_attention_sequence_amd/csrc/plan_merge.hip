@@ -60,6 +60,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, Plan
     seg_off[s + 1] = run;
   }
   if (t == 0) seg_off[0] = 0;
+  if (t < 4) hdr->zero[t] = 0;
   if (t == 1023) {
     int total = sums[1023];
     hdr->total = total;

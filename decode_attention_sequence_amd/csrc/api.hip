@@ -76,7 +76,9 @@ dcp_status_t run_attention(const dcp_attn_desc_t* d, const void* q, const void* 
   if (d->num_cache_blocks == 0) m.width = 0;
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
   WorkspaceView ws = carve_workspace(workspace, S, G, d->num_q_heads, d->v_dim);
-  if (launch_plan(m, S, G, ws, stream) != hipSuccess) return DCP_ERR_HIP;
+  // Fixed work per piece of a segment, in blocks (about 128 tokens' worth).
+  const int seg_cost = (128 + d->block_size - 1) / d->block_size;
+  if (launch_plan(m, S, G, seg_cost, ws, stream) != hipSuccess) return DCP_ERR_HIP;
   AttnLaunch L{d, q, k, v, kv_scale, m, S, ws};
   if (attn_begin && hipEventRecord(attn_begin, stream) != hipSuccess) return DCP_ERR_HIP;
   hipError_t err = d->kv_kind == DCP_KV_LATENT ? launch_mla(L, stream) : launch_gqa(L, stream);

@@ -40,13 +40,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 // the concatenation. Slots used <= S + G - 1.
 // ---------------------------------------------------------------------------
 struct PlanHeader {
-  int32_t chunk;  // blocks per work group (>= 1)
   int32_t total;  // blocks over all segments
-  int32_t pad[2];
+  int32_t pad[3];
   int32_t zero[4];  // 16 zero bytes: copy source for tile rows without a token
 };
-// Workspace layout: PlanHeader, seg_off[S + 1] (int32), then at 256-byte
-// alignment lse slots [num_slots, Hq] fp32, then o slots [num_slots, Hq, v_dim] fp32.
+// Workspace layout: PlanHeader, seg_off[S + 1], cost_off[S + 1] and
+// wg_start[G + 1] (int32), then at 256-byte alignment lse slots
+// [num_slots, Hq] fp32, then o slots [num_slots, Hq, v_dim] fp32.
 
 struct SegMap {
   const int32_t* table;  // [B, width]
@@ -111,6 +111,18 @@ __device__ __forceinline__ int find_segment(const int32_t* seg_off, int S, int x
   return lo;
 }
 
+// Work group whose block range holds concatenated block x: the last g in
+// [0, G) with wg_start[g] <= x (ranges are consecutive; empty ones share their
+// start with the next range).
+__device__ __forceinline__ int wg_of(const int32_t* wg_start, int G, int x) {
+  int lo = 0, hi = G;  // answer in [0, G)
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (wg_start[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 // Logical work-group index with consecutive ranges kept on one XCD: hardware
 // dispatches work group i to XCD i % 8, so groups that share a sequence (and
 // its query rows) read them through the same L2.
@@ -142,7 +154,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // ---------------------------------------------------------------------------
 struct WorkspaceView {
   PlanHeader* header;
-  int32_t* seg_off;
+  int32_t* seg_off;   // [S + 1] first concatenated block of each segment
+  int32_t* cost_off;  // [S + 1] planning scratch: cost prefix sums
+  int32_t* wg_start;  // [G + 1] first block of each work group's range
   float* lse;
   float* o;
   int num_slots;
@@ -151,7 +165,8 @@ struct WorkspaceView {
 size_t workspace_bytes_for(int S, int G, int Hq, int v_dim);
 WorkspaceView carve_workspace(void* ws, int S, int G, int Hq, int v_dim);
 
-hipError_t launch_plan(const SegMap& m, int S, int G, WorkspaceView ws, hipStream_t stream);
+hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, WorkspaceView ws,
+                       hipStream_t stream);
 hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, int G, int Hq, int v_dim,
                                void* out, dcp_dtype_t out_dtype, float* lse_out,
                                hipStream_t stream);

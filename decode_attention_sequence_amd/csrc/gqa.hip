@@ -32,6 +32,7 @@ struct GqaArgs {
   const char* v;
   SegMap map;
   const PlanHeader* hdr;
+  const int32_t* wg_start;  // [G + 1] block range of each work group
   const int32_t* seg_off;
   float* ws_o;
   float* ws_lse;
@@ -71,9 +72,8 @@ __global__ __launch_bounds__(64) void gqa_bf16_kernel(GqaArgs a) {
   const int q4 = lane >> 4, l16 = lane & 15;
   const int kvh = blockIdx.y;
   const int g = xcd_logical_group(blockIdx.x, a.G);
-  const int chunk = a.hdr->chunk, total = a.hdr->total;
-  int pos = g * chunk;
-  const int end = min(pos + chunk, total);
+  int pos = a.wg_start[g];
+  const int end = a.wg_start[g + 1];
   if (pos >= end) return;
   int s = find_segment(a.seg_off, a.S, pos);
   const int bs = a.map.bs;
@@ -252,9 +252,8 @@ __global__ __launch_bounds__(64) void gqa_f32_kernel(GqaArgs a) {
   const int lane = threadIdx.x;
   const int kvh = blockIdx.y;
   const int g = xcd_logical_group(blockIdx.x, a.G);
-  const int chunk = a.hdr->chunk, total = a.hdr->total;
-  int pos = g * chunk;
-  const int end = min(pos + chunk, total);
+  int pos = a.wg_start[g];
+  const int end = a.wg_start[g + 1];
   if (pos >= end) return;
   int s = find_segment(a.seg_off, a.S, pos);
   const int bs = a.map.bs;
@@ -373,6 +372,7 @@ hipError_t launch_gqa(const AttnLaunch& L, hipStream_t stream) {
   a.v = static_cast<const char*>(L.v_cache);
   a.map = L.map;
   a.hdr = L.ws.header;
+  a.wg_start = L.ws.wg_start;
   a.seg_off = L.ws.seg_off;
   a.ws_o = L.ws.o;
   a.ws_lse = L.ws.lse;

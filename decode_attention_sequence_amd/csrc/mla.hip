@@ -82,6 +82,7 @@ struct MlaArgs {
   const char* kv_scale;   // fp8: fp32 [num_cache_blocks, bs]
   SegMap map;
   const PlanHeader* hdr;
+  const int32_t* wg_start;  // [G + 1] block range of each work group
   const int32_t* seg_off;
   float* ws_o;
   float* ws_lse;
@@ -309,10 +310,8 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
   const int l16 = lane & 15;
   const int g = xcd_logical_group(blockIdx.x, kGroups);
   const int head0 = blockIdx.y * 16 * HG;
-  const int chunk = a.hdr->chunk;
-  const int total = a.hdr->total;
-  int pos = g * chunk;
-  const int end = min(pos + chunk, total);
+  int pos = a.wg_start[g];
+  const int end = a.wg_start[g + 1];
   if (pos >= end) return;
   int s = find_segment(a.seg_off, a.S, pos);
   const int bs = a.map.bs;
@@ -738,6 +737,12 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
 //    tile table in LDS, and segment boundaries inside a window are handled
 //    per tile (state reset, query reload, result store) without draining the
 //    copy pipeline.
+#ifndef PP_SSPREAD
+#define PP_SSPREAD 18
+#endif
+#ifndef PP_VSPREAD
+#define PP_VSPREAD 8
+#endif
 struct PP {
   static constexpr int kMT = 8;                           // 16-column M tiles per value wave
   static constexpr int kPerWave = (kDmaInst + 7) / 8;     // copies per wave and tile (at most)
@@ -745,6 +750,10 @@ struct PP {
   static constexpr int kSDist = 3;                        // score K steps of fragments read ahead
   static constexpr int kSRing = kSDist + 2;
   static constexpr int kPD = 4;                           // value M tiles of reads in flight
+  // Copies of tile t + 2 go out one by one over the first kSSpread score K
+  // steps / kVSpread value M tiles.
+  static constexpr int kSSpread = PP_SSPREAD;
+  static constexpr int kVSpread = PP_VSPREAD;
   static constexpr int kMaxPieces = 32;                   // segments per window
   static constexpr int kMaxTiles = 640;                   // tiles per window
   static constexpr int kRingB = kStages * kTileB;
@@ -794,8 +803,8 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   const int g = xcd_logical_group(blockIdx.x, kGroups);
   const int head0 = blockIdx.y * 64;
   const int total = a.hdr->total;
-  const int range0 = g * a.hdr->chunk;
-  const int end = min(range0 + a.hdr->chunk, total);
+  const int range0 = a.wg_start[g];
+  const int end = a.wg_start[g + 1];
   if (range0 >= end) return;
   const int bs = a.map.bs;
   const int D = a.map.D;
@@ -1061,8 +1070,8 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
               s1a = E::mfma(rb[kk % PP::kSRing], qv, s1a);
             }
             // copies n in [n0, n1) go out after this K step
-            constexpr int n0 = kk * PP::kPerWave / kKSteps;
-            constexpr int n1 = (kk + 1) * PP::kPerWave / kKSteps;
+            constexpr int n0 = kk < PP::kSSpread ? kk * PP::kPerWave / PP::kSSpread : PP::kPerWave;
+            constexpr int n1 = kk < PP::kSSpread ? (kk + 1) * PP::kPerWave / PP::kSSpread : PP::kPerWave;
             if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + 2); });
           });
           const f32x4 sv0 = s0a + s0b, sv1 = s1a + s1b;
@@ -1169,8 +1178,8 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
               constexpr int nt = decltype(nc)::value;
               st[4 * mt + nt] = E::mfma(av, __builtin_bit_cast(bf16x8, pb[nt]), st[4 * mt + nt]);
             });
-            constexpr int n0 = mt * PP::kPerWave / PP::kMT;
-            constexpr int n1 = (mt + 1) * PP::kPerWave / PP::kMT;
+            constexpr int n0 = mt < PP::kVSpread ? mt * PP::kPerWave / PP::kVSpread : PP::kPerWave;
+            constexpr int n1 = mt < PP::kVSpread ? (mt + 1) * PP::kPerWave / PP::kVSpread : PP::kPerWave;
             if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + 2); });
           });
           const TileInfo ti = tile_info(kv);
@@ -1240,6 +1249,7 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   a.kv_scale = reinterpret_cast<const char*>(L.kv_scale);
   a.map = L.map;
   a.hdr = L.ws.header;
+  a.wg_start = L.ws.wg_start;
   a.seg_off = L.ws.seg_off;
   a.ws_o = L.ws.o;
   a.ws_lse = L.ws.lse;

@@ -15,9 +15,14 @@ namespace dcp {
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+static inline size_t plan_bytes(int S, int G) {
+  return sizeof(PlanHeader) +
+         sizeof(int32_t) * (2 * (static_cast<size_t>(S) + 1) + static_cast<size_t>(G) + 1);
+}
+
 size_t workspace_bytes_for(int S, int G, int Hq, int v_dim) {
   size_t slots = static_cast<size_t>(S) + static_cast<size_t>(G) - 1;
-  size_t off = align_up(sizeof(PlanHeader) + sizeof(int32_t) * (static_cast<size_t>(S) + 1), 256);
+  size_t off = align_up(plan_bytes(S, G), 256);
   off += align_up(slots * Hq * sizeof(float), 256);
   off += slots * Hq * v_dim * sizeof(float);
   return off;
@@ -29,7 +34,9 @@ WorkspaceView carve_workspace(void* ws, int S, int G, int Hq, int v_dim) {
   v.num_slots = S + G - 1;
   v.header = reinterpret_cast<PlanHeader*>(base);
   v.seg_off = reinterpret_cast<int32_t*>(base + sizeof(PlanHeader));
-  size_t off = align_up(sizeof(PlanHeader) + sizeof(int32_t) * (static_cast<size_t>(S) + 1), 256);
+  v.cost_off = v.seg_off + S + 1;
+  v.wg_start = v.cost_off + S + 1;
+  size_t off = align_up(plan_bytes(S, G), 256);
   v.lse = reinterpret_cast<float*>(base + off);
   off += align_up(static_cast<size_t>(v.num_slots) * Hq * sizeof(float), 256);
   v.o = reinterpret_cast<float*>(base + off);
@@ -37,39 +44,77 @@ WorkspaceView carve_workspace(void* ws, int S, int G, int Hq, int v_dim) {
 }
 
 // ------------------------------------------------------------------ planning
-__global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, PlanHeader* hdr,
-                                                    int32_t* seg_off) {
+// Stream-K split weighted by cost: a non-empty segment costs its blocks plus
+// seg_cost blocks' worth of fixed work (starting a piece, storing its
+// partial), so a work group whose range crosses many short segments gets
+// fewer blocks. Work group g takes the blocks whose cost positions fall in
+// [g cc, (g + 1) cc), cc = ceil(total cost / G); a segment's overhead units
+// come before its first block.
+__global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int seg_cost,
+                                                    PlanHeader* hdr, int32_t* seg_off,
+                                                    int32_t* cost_off, int32_t* wg_start) {
   __shared__ int sums[1024];
+  __shared__ int costs[1024];
   const int t = threadIdx.x;
   const int per = (S + 1023) / 1024;
   const int s0 = t * per;
   const int s1 = min(S, s0 + per);
-  int local = 0;
-  for (int s = s0; s < s1; ++s) local += segment_blocks(m, s);
+  int local = 0, local_c = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int nb = segment_blocks(m, s);
+    local += nb;
+    local_c += nb + (nb > 0 ? seg_cost : 0);
+  }
   sums[t] = local;
+  costs[t] = local_c;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    int v = t >= off ? sums[t - off] : 0;
+    const int v = t >= off ? sums[t - off] : 0;
+    const int vc = t >= off ? costs[t - off] : 0;
     __syncthreads();
     sums[t] += v;
+    costs[t] += vc;
     __syncthreads();
   }
-  int run = sums[t] - local;
+  int run = sums[t] - local, run_c = costs[t] - local_c;
   for (int s = s0; s < s1; ++s) {
-    run += segment_blocks(m, s);
+    const int nb = segment_blocks(m, s);
+    run += nb;
+    run_c += nb + (nb > 0 ? seg_cost : 0);
     seg_off[s + 1] = run;
+    cost_off[s + 1] = run_c;
   }
-  if (t == 0) seg_off[0] = 0;
+  if (t == 0) {
+    seg_off[0] = 0;
+    cost_off[0] = 0;
+  }
   if (t < 4) hdr->zero[t] = 0;
-  if (t == 1023) {
-    int total = sums[1023];
-    hdr->total = total;
-    hdr->chunk = max(1, (total + G - 1) / G);
+  const int total = sums[1023];
+  const int total_c = costs[1023];
+  if (t == 0) hdr->total = total;
+  __syncthreads();  // seg_off and cost_off complete
+  const long long cc = max(1, (total_c + G - 1) / G);
+  for (int g = t; g <= G; g += 1024) {
+    const long long y = min(static_cast<long long>(g) * cc, static_cast<long long>(total_c));
+    // last segment s < S with cost_off[s] <= y
+    int lo = 0, hi = S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cost_off[mid] <= y) lo = mid; else hi = mid;
+    }
+    int x = total;
+    if (S > 0 && y < cost_off[lo + 1]) {
+      const long long o = y - cost_off[lo] - seg_cost;  // blocks of segment lo before y
+      x = seg_off[lo] + static_cast<int>(max(0ll, o));
+    }
+    wg_start[g] = g == 0 ? 0 : x;
   }
 }
 
-hipError_t launch_plan(const SegMap& m, int S, int G, WorkspaceView ws, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, m, S, G, ws.header, ws.seg_off);
+hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, WorkspaceView ws,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, m, S, G, seg_cost, ws.header,
+                     ws.seg_off, ws.cost_off, ws.wg_start);
   return hipGetLastError();
 }
 
@@ -77,15 +122,15 @@ hipError_t launch_plan(const SegMap& m, int S, int G, WorkspaceView ws, hipStrea
 // Slot sources: which stored partial rows feed output row b.
 struct PieceSource {
   const int32_t* seg_off;
-  const PlanHeader* hdr;
+  const int32_t* wg_start;
+  int G;
   int D;
   template <class F>
   __device__ __forceinline__ void for_each(int b, F&& f) const {
-    const int chunk = hdr->chunk;
     for (int s = b * D; s < (b + 1) * D; ++s) {
       int a = seg_off[s], e = seg_off[s + 1];
       if (a >= e) continue;
-      for (int g = a / chunk, g1 = (e - 1) / chunk; g <= g1; ++g) f(s + g);
+      for (int g = wg_of(wg_start, G, a), g1 = wg_of(wg_start, G, e - 1); g <= g1; ++g) f(s + g);
     }
   }
 };
@@ -152,8 +197,7 @@ static dim3 merge_block(int v_dim) {
 hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, int G, int Hq, int v_dim,
                                void* out, dcp_dtype_t out_dtype, float* lse_out,
                                hipStream_t stream) {
-  (void)G;
-  PieceSource src{ws.seg_off, ws.header, m.D};
+  PieceSource src{ws.seg_off, ws.wg_start, G, m.D};
   dim3 block = merge_block(v_dim);
   int hpb = block.x / (v_dim / 4);
   dim3 grid(m.batch, (Hq + hpb - 1) / hpb);

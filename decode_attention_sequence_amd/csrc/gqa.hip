@@ -117,6 +117,7 @@ __global__ __launch_bounds__(64) void gqa_bf16_kernel(GqaArgs a) {
 #pragma unroll
     for (int mt = 0; mt < kVTiles; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    float l_rnd = 0.f;  // the same sum over the probabilities as rounded to bf16
     const int ntiles = (p.ntok + kT - 1) / kT;
 
     auto load_id = [&](int tau0) -> int {
@@ -202,10 +203,13 @@ __global__ __launch_bounds__(64) void gqa_bf16_kernel(GqaArgs a) {
         const float p1 = fast_exp2(x[2 * i + 1] - m_use);
         const uint16_t b0 = f32_to_bf16_bits(p0);
         const uint16_t b1 = f32_to_bf16_bits(p1);
-        psum += p0 + p1;  // the normaliser keeps the fp32 probabilities
+        psum += p0 + p1;  // (the LSE's sum keeps the fp32 probabilities)
         pk[i] = static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16);
       }
       l_run = l_run * alpha + psum;
+      l_rnd = l_rnd * alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_rnd = add_bf16x2(pk[i], l_rnd);
       const i32x4 pki = {static_cast<int>(pk[0]), static_cast<int>(pk[1]), static_cast<int>(pk[2]),
                          static_cast<int>(pk[3])};
       const bf16x8 pb = __builtin_bit_cast(bf16x8, pki);
@@ -224,7 +228,11 @@ __global__ __launch_bounds__(64) void gqa_bf16_kernel(GqaArgs a) {
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // The output is normalised by the sum of the bf16 probabilities its
+    // product used; the LSE takes the fp32 sum.
+    float l_out = l_rnd + __shfl_xor(l_rnd, 16);
+    l_out += __shfl_xor(l_out, 32);
+    const float inv = l_out > 0.f ? 1.f / l_out : 0.f;
     const float lse = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
     const size_t slot = static_cast<size_t>(s) + g;
     if (head_ok) {

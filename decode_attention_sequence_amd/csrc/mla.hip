@@ -178,7 +178,6 @@ __device__ __forceinline__ void wait_vm() {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // e4m3 codes -> fp16, exact: every e4m3 value (4 significant bits, |x| <= 448,
 // down to 2^-9) is an fp16 normal or subnormal number.
@@ -249,25 +248,27 @@ struct Cfg {
   static constexpr int kF16Off = 0;                            // fp8: two fp16 tiles
   static constexpr int kPOff = FP8 ? 2 * kTileB : 0;
   static constexpr int kMxOff = kPOff + HG * 64 * 16;          // [2][16][4] floats
-  static constexpr int kLsumOff = kMxOff + 2 * 16 * 4 * 4;     // [2][64] floats
-  static constexpr int kIdsOff = kLsumOff + 2 * 64 * 4;
+  static constexpr int kLsumOff = kMxOff + 2 * 16 * 4 * 4;     // [2][2][64] floats
+  static constexpr int kIdsOff = kLsumOff + 4 * 64 * 4;
   static constexpr int kFlagOff = kIdsOff + kIdWin * 4;        // one byte per wave
   static constexpr int kAuxB = kFlagOff + 16;
   static_assert(kRingB + kAuxB <= 160 * 1024, "LDS budget");
 };
 
-// Wait until at most n_after tiles (C::kOps operations each) issued after the
+// Wait until at most n_after tiles (OPS operations each) issued after the
 // awaited one are still in flight. The hardware counter saturates at 63, so
 // larger counts are clamped, which only waits for more.
-template <int OPS>
+// MAXN: the largest n_after a caller passes (larger values wait as for MAXN).
+template <int OPS, int MAXN = 2>
 __device__ __forceinline__ void wait_tiles_after_n(int n_after) {
+  static_assert(MAXN >= 1 && MAXN <= 3, "one to three later tiles");
   constexpr int k1 = OPS > 63 ? 63 : OPS;
   constexpr int k2 = 2 * OPS > 63 ? 63 : 2 * OPS;
-  switch (n_after) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<k1>(); break;
-    default: wait_vm<k2>(); break;
-  }
+  constexpr int k3 = 3 * OPS > 63 ? 63 : 3 * OPS;
+  if (n_after <= 0) wait_vm<0>();
+  else if (MAXN == 1 || n_after == 1) wait_vm<k1>();
+  else if (MAXN == 2 || n_after == 2) wait_vm<k2>();
+  else wait_vm<k3>();
 }
 
 // Location of copy slot `slot` of a tile: row and logical 16-byte chunk.
@@ -379,6 +380,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
 #pragma unroll
     for (int nt = 0; nt < HG; ++nt) m_ref[nt] = -INFINITY;
     float l_run = 0.f;  // sum of this lane's probabilities for head h_s
+    float l_rnd = 0.f;  // bf16: the same sum over the probabilities as rounded for P^T
 
     // Windows of at most kIdWin blocks share one LDS copy of their block ids.
     for (int wb = p.i0; wb < p.i1; wb += kIdWin) {
@@ -592,11 +594,17 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
         float hmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         hmax = max_xor32(max_xor16(hmax));
         // P^T fragment half of this wave: tokens 16th + 4q4 + i of head h_s.
-        auto store_p = [&](const float* pv) {
+        auto store_p = [&](const float* pv) -> i32x2 {
           const uint32_t lo = E::pack2(FP8 ? pv[0] * sig[0] : pv[0], FP8 ? pv[1] * sig[1] : pv[1]);
           const uint32_t hi = E::pack2(FP8 ? pv[2] * sig[2] : pv[2], FP8 ? pv[3] * sig[3] : pv[3]);
-          *reinterpret_cast<DCP_LDS i32x2*>(aux + C::kPOff + ((hg * 64 + lane) * 2 + th) * 8) =
-              i32x2{static_cast<int>(lo), static_cast<int>(hi)};
+          const i32x2 pk = {static_cast<int>(lo), static_cast<int>(hi)};
+          *reinterpret_cast<DCP_LDS i32x2*>(aux + C::kPOff + ((hg * 64 + lane) * 2 + th) * 8) = pk;
+          return pk;
+        };
+        // bf16: the rounded probabilities' sum, for the output normalisation
+        auto add_rounded = [&](i32x2 pk, float c) -> float {
+          if constexpr (FP8) return c;
+          return add_bf16x2(static_cast<uint32_t>(pk[1]), add_bf16x2(static_cast<uint32_t>(pk[0]), c));
         };
         // bf16 cache: probabilities may reach 2^8 before the reference max of a
         // head is raised. fp8 cache: it is raised on any increase, so p <= 1
@@ -615,7 +623,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
           const float m_use = m_own == -INFINITY ? 0.f : m_own;
 #pragma unroll
           for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m_use);
-          store_p(p);
+          const i32x2 pk = store_p(p);
           const bool need = __ballot(hmax > m_own + kRaise) != 0ull;
           // (The vote is written and read with explicit-wait asm: as plain LDS
           // accesses the compiler waits for every in-flight copy first.)
@@ -625,7 +633,10 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
           lds_b64<0>(votes, flags_addr);
           wait_lgkm<0>(votes);
           slow = wave_uniform((votes[0] | votes[1]) != 0);
-          if (!slow) l_run += (p[0] + p[1]) + (p[2] + p[3]);
+          if (!slow) {
+            l_run += (p[0] + p[1]) + (p[2] + p[3]);
+            l_rnd = add_rounded(pk, l_rnd);
+          }
         }
         if (slow) {  // some wave votes for a raise (always, for fp8)
           if (q4 == 0) mx[(th * 16 + l16) * 4 + hg] = hmax;
@@ -655,7 +666,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m_use);
           l_run = l_run * a_own + ((p[0] + p[1]) + (p[2] + p[3]));
-          store_p(p);
+          l_rnd = add_rounded(store_p(p), l_rnd * a_own);
           lds_barrier();
           if (__ballot(any_raise)) {
 #pragma unroll
@@ -701,14 +712,21 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
     }
 
     // ---- finalise the piece: normalise and store (O, LSE) in slot s + g
+    // (bf16: the output is normalised by the rounded probabilities' sum, the
+    // LSE takes the fp32 sum)
     const float l_h = sum_xor32(sum_xor16(l_run));
-    if (q4 == 0) lsum[th * 64 + 16 * hg + l16] = l_h;
+    const float l_o = FP8 ? l_h : sum_xor32(sum_xor16(l_rnd));
+    if (q4 == 0) {
+      lsum[th * 64 + 16 * hg + l16] = l_h;
+      lsum[128 + th * 64 + 16 * hg + l16] = l_o;
+    }
     __syncthreads();
     const size_t slot = static_cast<size_t>(s) + g;
 #pragma unroll
     for (int nt = 0; nt < HG; ++nt) {
       const float l_tot = lsum[16 * nt + l16] + lsum[64 + 16 * nt + l16];
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float l_out = lsum[128 + 16 * nt + l16] + lsum[192 + 16 * nt + l16];
+      const float inv = l_out > 0.f ? 1.f / l_out : 0.f;
       float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) *reinterpret_cast<f32x4*>(orow + 16 * mt) = acc[mt][nt] * inv;
@@ -720,7 +738,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 cache, 64 heads per work group, blocks holding a multiple of 32 tokens:
+// 64 heads per work group, blocks holding a multiple of 32 tokens:
 // producer / consumer form with one barrier per tile.
 //  * Waves 0-3 ("score waves") own 16 heads each. For tile t they compute S^T
 //    over all 32 tokens, run the online softmax of their own heads (so no
@@ -729,44 +747,72 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
 //    and accumulate O^T += C^T . P^T for tile t - 1 in the same step.
 //  * Waves w and w + 4 share a SIMD, so one wave's softmax, LDS waits and
 //    copy issue overlap the other's MFMAs.
-//  * The copy ring holds tile t (scores), tile t - 1 (values) and the two
-//    tiles after t in flight; the copies of tile t + 2 go out during step t,
-//    spread over both kinds of waves' MFMA loops.
+//  * The copy ring holds tile t (scores), tile t - 1 (values) and the tiles
+//    after t in flight (two of 36 KB for bf16, four of 18 KB for fp8); the
+//    copies of the next tile go out during step t, spread over both kinds of
+//    waves' MFMA loops.
 //  * The tiles of a work group's whole range form one stream: a window of
 //    the range (up to kMaxTiles tiles of up to kMaxPieces segments) gets a
 //    tile table in LDS, and segment boundaries inside a window are handled
 //    per tile (state reset, query reload, result store) without draining the
 //    copy pipeline.
+//  * fp8 cache: each tile carries its 32 token scales. The codes are widened
+//    to fp16 in registers right after each LDS fragment read (exact; see
+//    f8x8_to_f16x8) and both products run on v_mfma_f32_16x16x32_f16. A score
+//    lane reads one 16-byte chunk of its row per read, which covers two K
+//    steps (the query fragments are loaded in the same column order); a value
+//    lane reads its eight tokens of one column pair with ds_read_b64_tr_b8,
+//    one read per M tile. The token scale multiplies the fp32 score and the
+//    probability that weights the token's value (rounded to fp16).
+template <bool FP8>
 struct PP {
-  static constexpr int kMT = 8;                           // 16-column M tiles per value wave
-  static constexpr int kPerWave = (kDmaInst + 7) / 8;     // copies per wave and tile (at most)
-  static constexpr int kHiWaves = kDmaInst % 8 ? kDmaInst % 8 : 8;  // copy groups with kPerWave
-  static constexpr int kSDist = 3;                        // score K steps of fragments read ahead
+  static constexpr int kRowBytes = FP8 ? kF8RowB : kRowB;    // cache row bytes in LDS
+  static constexpr int kCodeB = FP8 ? kF8TileB : kTileB;     // tile bytes without scales
+  static constexpr int kInst = FP8 ? kF8DmaInst : kDmaInst;  // wave-wide 16-byte copies per tile
+  static constexpr int kScaleOff = kCodeB;                   // fp8: token scales of the tile
+  static constexpr int kStageB = FP8 ? kCodeB + 256 : kCodeB;
+  static constexpr int kStages = FP8 ? 6 : 4;                // ring stages
+  static constexpr int kAhead = kStages - 2;                 // tiles copied ahead of the scores
+  static constexpr int kMT = 8;                              // 16-column M tiles per value wave
+  static constexpr int kPerWave = (kInst + 7) / 8;           // copy rounds per tile (at most)
+  // Copy groups cw < kCodeHi issue kPerWave code copies per tile, the others
+  // one fewer; for fp8 group kCodeHi also copies the tile's token scales.
+  static constexpr int kCodeHi = kInst % 8 ? kInst % 8 : 8;
+  static constexpr int kHiWaves = FP8 ? kCodeHi + 1 : kCodeHi;  // groups with kPerWave operations
+  static constexpr int kSteps = FP8 ? kKSteps / 2 : kKSteps;    // score fragment reads per M tile
+  static constexpr int kSDist = 3;                           // score reads in flight (per M tile)
   static constexpr int kSRing = kSDist + 2;
-  static constexpr int kPD = 4;                           // value M tiles of reads in flight
-  static_assert(2 + 1 + 4 + 2 * kPD <= 15, "LDS reads in flight exceed the lgkmcnt range");
-  // Copies of tile t + 2 go out one by one over the first kSSpread score K
-  // steps / kVSpread value M tiles.
-  static constexpr int kSSpread = kKSteps;
+  static constexpr int kPD = FP8 ? 8 : 4;                    // value M tiles of reads in flight
+  static constexpr int kPReads = FP8 ? 1 : 2;                // LDS reads per value M tile
+  static_assert(2 + 1 + 4 + kPReads * kPD <= 15, "LDS reads in flight exceed the lgkmcnt range");
+  static_assert(2 + 2 + 2 * kSDist <= 15, "LDS reads in flight exceed the lgkmcnt range");
+  // Copies of the next tile go out one by one over the first kSSpread score
+  // reads / kVSpread value M tiles.
+  static constexpr int kSSpread = kSteps;
   static constexpr int kVSpread = kMT;
-  static constexpr int kMaxPieces = 32;                   // segments per window
-  static constexpr int kMaxTiles = 640;                   // tiles per window
-  static constexpr int kRingB = kStages * kTileB;
-  static constexpr int kPBufB = 4 * 64 * 16;              // P^T of one tile, 4 head groups
-  static constexpr int kPOff = 0;                         // [2] tiles
-  static constexpr int kAlphaOff = kPOff + 2 * kPBufB;    // [2][16 lanes][4 groups] floats
-  static constexpr int kFlagOff = kAlphaOff + 2 * 64 * 4; // [2][4] bytes
-  static constexpr int kFinOff = kFlagOff + 16;           // [2][64] head sums
-  static constexpr int kPieceOff = kFinOff + 2 * 64 * 4;  // [kMaxPieces] x 2 int4
+  // A head's reference max rises only when a tile's max exceeds it by more
+  // than this (log2 units): probabilities stay <= 2^kRaise. fp8 keeps it at
+  // 4 so that probability times token scale stays inside the fp16 range for
+  // scales below 4096.
+  static constexpr float kRaise = FP8 ? 4.f : 8.f;
+  static constexpr int kMaxPieces = 32;                      // segments per window
+  static constexpr int kMaxTiles = 640;                      // tiles per window
+  static constexpr int kRingB = kStages * kStageB;
+  static constexpr int kPBufB = 4 * 64 * 16;                 // P^T of one tile, 4 head groups
+  static constexpr int kPOff = 0;                            // [2] tiles
+  static constexpr int kAlphaOff = kPOff + 2 * kPBufB;       // [2][16 lanes][4 groups] floats
+  static constexpr int kFlagOff = kAlphaOff + 2 * 64 * 4;    // [2][4] bytes
+  static constexpr int kFinOff = kFlagOff + 16;              // [2][64] head sums
+  static constexpr int kPieceOff = kFinOff + 2 * 64 * 4;     // [kMaxPieces] x 2 int4
   static constexpr int kTileOff = kPieceOff + kMaxPieces * 32;  // [kMaxTiles] int2
   static constexpr int kMiscOff = kTileOff + kMaxTiles * 8;     // tiles, window end
   static constexpr int kAuxB = kMiscOff + 16;
   static_assert(kRingB + kAuxB <= 160 * 1024, "LDS budget");
 };
-// Tile table entry: x = block id (-1: unusable, the tile reads the safe
-// address and is zeroed), y = tile offset in the block / 32 (bits 0-7),
-// valid rows - 1 (bits 8-15), piece (bits 16-23), first tile of its segment
-// (bit 30), last tile of its segment (bit 31).
+// Tile table entry: x = block id (-1: unusable, the tile's rows read zeros),
+// y = tile offset in the block / 32 (bits 0-7), valid rows - 1 (bits 8-15),
+// piece (bits 16-23), first tile of its segment (bit 30), last tile of its
+// segment (bit 31).
 // Piece entry: {s, b, first local block, -}, {first tile, tiles, tokens, -}.
 
 __device__ __forceinline__ void lds_store_b32(uint32_t addr, float v) {
@@ -779,11 +825,41 @@ template <int OFF>
 __device__ __forceinline__ void lds_b32(int& r, uint32_t addr) {
   asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
 }
+// Transposed 8-bit read: within each 16-lane group, lanes 2k and 2k + 1 give
+// the addresses of bytes 0-7 and 8-15 of row k (k = 0..7), and lane m
+// receives byte m of each of the eight rows.
+template <int OFF>
+__device__ __forceinline__ void lds_tr8(i32x2& r, uint32_t addr) {
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+}
 
+// fp8 rows in LDS (576 bytes, 36 chunks of 16 bytes): logical chunk c of row
+// r sits at (c & ~3) | ((c & 3) ^ f8_swz(r)). Both read patterns -- 16 rows x
+// one chunk (score fragments) and 32 rows x one chunk (transposed value
+// fragments, rows {4q + k, 16 + 4q + k} per 16-lane group q) -- then spread
+// over all 64 banks.
+__device__ __forceinline__ int f8_swz(int r) { return ((r >> 2) & 3) ^ ((r >> 3) & 2); }
+
+// Eight e4m3 codes (two dwords, byte order) -> eight fp16 values, exact:
+// every e4m3 number (4 significant bits, |x| <= 448, down to 2^-9) is an fp16
+// normal or subnormal number.
+__device__ __forceinline__ i32x4 f8x8_to_f16x8(int d0, int d1) {
+  const auto h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<unsigned>(d0), 1.f, false);
+  const auto h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<unsigned>(d0), 1.f, true);
+  const auto h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<unsigned>(d1), 1.f, false);
+  const auto h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<unsigned>(d1), 1.f, true);
+  return i32x4{__builtin_bit_cast(int, h0), __builtin_bit_cast(int, h1), __builtin_bit_cast(int, h2),
+               __builtin_bit_cast(int, h3)};
+}
+
+template <bool FP8>
 __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
-  using E = Elt<false>;
-  __shared__ __attribute__((aligned(16))) char ring_raw[PP::kRingB];
-  __shared__ __attribute__((aligned(16))) char aux_raw[PP::kAuxB];
+  using E = Elt<FP8>;
+  using P = PP<FP8>;
+  constexpr int kStages = P::kStages;
+  constexpr int kAhead = P::kAhead;
+  __shared__ __attribute__((aligned(16))) char ring_raw[P::kRingB];
+  __shared__ __attribute__((aligned(16))) char aux_raw[P::kAuxB];
   DCP_LDS char* ring = (DCP_LDS char*)ring_raw;
   DCP_LDS char* aux = (DCP_LDS char*)aux_raw;
   const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
@@ -807,34 +883,63 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   // Copies: copy group cw issues slots cw + 8n of a tile. The value waves take
   // the groups with the extra copy (their MFMA loop has more room for them).
   const int cw = (w + 4) & 7;
-  const bool hi_wave = cw < PP::kHiWaves;
-  int32_t cp_off[PP::kPerWave];
-  int cp_row[PP::kPerWave];  // tile row this lane's copy n fills
+  const bool hi_wave = cw < P::kHiWaves;
+  int32_t cp_off[P::kPerWave];
+  int cp_row[P::kPerWave];  // tile row this lane's copy n fills
 #pragma unroll
-  for (int n = 0; n < PP::kPerWave; ++n) {
+  for (int n = 0; n < P::kPerWave; ++n) {
     const int ii = cw + 8 * n;
     int row = 0, c = 0;
-    if (ii < kDmaInst) slot_row_chunk<false>(ii * 64 + lane, row, c);
+    if (ii < P::kInst) {
+      if constexpr (FP8) {
+        const int slot = ii * 64 + lane;
+        row = slot / kF8RowCh;
+        const int pc = slot - row * kF8RowCh;
+        c = (pc & ~3) | ((pc & 3) ^ f8_swz(row));
+      } else {
+        slot_row_chunk<false>(ii * 64 + lane, row, c);
+      }
+    }
     cp_off[n] = static_cast<int32_t>(row * a.token_stride_b) + 16 * c;
     cp_row[n] = row;
   }
   auto wait_tiles = [&](int n_after) {
-    if (hi_wave) wait_tiles_after_n<PP::kPerWave>(n_after);
-    else wait_tiles_after_n<PP::kPerWave - 1>(n_after);
+    if (hi_wave) wait_tiles_after_n<P::kPerWave, kAhead - 1>(n_after);
+    else wait_tiles_after_n<P::kPerWave - 1, kAhead - 1>(n_after);
   };
 
-  // Score waves: A fragments of M tile 0 (row l16) and 1 (row 16 + l16),
-  // chunk 4kk + q4 (even kk) or 4 + 4(kk - 1) + q4 (odd kk).
+  // Score waves: A fragments of M tile 0 (row l16) and 1 (row 16 + l16).
+  // bf16: chunk 4kk + q4 (even kk) or 4 + 4(kk - 1) + q4 (odd kk), one K step
+  // per read. fp8: chunk 4j + q4 of read j, i.e. columns 64j + 16q4 .. +15,
+  // K steps 2j (first 8 codes) and 2j + 1 (last 8).
   const int r0 = l16, r1 = 16 + l16;
-  const uint32_t a0e = r0 * kRowB + 16 * (q4 ^ swz(r0));
-  const uint32_t a0o = r0 * kRowB + 16 * ((4 + q4) ^ swz(r0));
-  const uint32_t a1e = r1 * kRowB + 16 * (q4 ^ swz(r1));
-  const uint32_t a1o = r1 * kRowB + 16 * ((4 + q4) ^ swz(r1));
-  // Value waves: transposed A fragments, lane (k = l16 / 4, m = l16 % 4) at rows
-  // 4q4 + k and 16 + 4q4 + k, columns vbase + 16mt + 4m .. +3.
+  uint32_t a0e, a0o, a1e, a1o;
+  if constexpr (FP8) {
+    a0e = a0o = r0 * kF8RowB + 16 * (q4 ^ f8_swz(r0));
+    a1e = a1o = r1 * kF8RowB + 16 * (q4 ^ f8_swz(r1));
+  } else {
+    a0e = r0 * kRowB + 16 * (q4 ^ swz(r0));
+    a0o = r0 * kRowB + 16 * ((4 + q4) ^ swz(r0));
+    a1e = r1 * kRowB + 16 * (q4 ^ swz(r1));
+    a1o = r1 * kRowB + 16 * ((4 + q4) ^ swz(r1));
+  }
+  // Value waves: transposed A fragments of value columns vbase + 16mt ..
+  // +15 over the tokens 4q4 + k and 16 + 4q4 + k (k = 0..3), the order in
+  // which the score waves' MFMA results hold them.
+  //  bf16: lane (k = l16 / 4, m = l16 % 4) at rows 4q4 + k and 16 + 4q4 + k,
+  //        columns vbase + 16mt + 4m .. +3 (two reads per M tile);
+  //  fp8:  lane j = l16 at row T(j / 2) (T(k) = 4q4 + k, then 16 + 4q4 + k - 4),
+  //        bytes 8(j % 2) .. +7 of chunk vbase / 16 + mt (one read per M tile).
   const int vbase = 128 * grp;
-  uint32_t t_off[8];
-  {
+  constexpr int kTOff = FP8 ? 4 : 8;
+  uint32_t t_off[kTOff];
+  if constexpr (FP8) {
+    const int k = l16 >> 1;
+    const int row = k < 4 ? 4 * q4 + k : 16 + 4 * q4 + k - 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      t_off[j] = row * kF8RowB + 16 * (vbase / 16 + (j ^ f8_swz(row))) + 8 * (l16 & 1);
+  } else {
     const int t_k = l16 >> 2, t_m = l16 & 3;
     const int t_row0 = 4 * q4 + t_k, t_row1 = 16 + 4 * q4 + t_k;
     const int cgrp = 128 * (vbase / 64);
@@ -845,9 +950,9 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
       t_off[4 + j] = cgrp + t_row1 * kRowB + 16 * (c ^ swz(t_row1)) + 8 * (t_m & 1);
     }
   }
-  const uint32_t flags_addr = aux_addr + PP::kFlagOff;
-  const uint32_t tiles_addr = aux_addr + PP::kTileOff;
-  const uint32_t piece_addr = aux_addr + PP::kPieceOff;
+  const uint32_t flags_addr = aux_addr + P::kFlagOff;
+  const uint32_t tiles_addr = aux_addr + P::kTileOff;
+  const uint32_t piece_addr = aux_addr + P::kPieceOff;
 
   // Tile table entry t of the current window (wave-uniform).
   struct TileInfo {
@@ -885,27 +990,40 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
     wait_lgkm<0>(v);
     return wave_uniform(v);
   };
-  // Copy source of a tile: its block's rows, and for rows that hold no real
-  // token of a usable block, 16 zero bytes of the workspace instead (so no
-  // tile ever needs zeroing in LDS).
+  // Copy source of a tile: its block's rows (and, for fp8, token scales), and
+  // for rows that hold no real token of a usable block, 16 zero bytes of the
+  // workspace instead (so no tile ever needs zeroing in LDS).
   struct Src {
     const char* base;
-    int nvalid;  // rows taken from the block
+    const char* sbase;  // fp8: scale of the tile's first token
+    int nvalid;         // rows taken from the block
   };
   auto tile_src = [&](const TileInfo& ti) -> Src {
-    if (ti.id < 0) return Src{a.kv, 0};
+    if (ti.id < 0) return Src{a.kv, a.kv_scale, 0};
+    const int tok0 = 32 * (ti.y & 0xff);
     return Src{a.kv + static_cast<long long>(ti.id) * a.block_stride_b +
-                   static_cast<long long>(32 * (ti.y & 0xff)) * a.token_stride_b,
-               ti.nvalid()};
+                   static_cast<long long>(tok0) * a.token_stride_b,
+               a.kv_scale + 4 * (static_cast<long long>(ti.id) * bs + tok0), ti.nvalid()};
   };
   auto copy_one = [&](auto nc, const Src& sr, int t) {
     constexpr int n = decltype(nc)::value;
     const int ii = cw + 8 * n;
-    if (n == PP::kPerWave - 1 && ii >= kDmaInst) return;
+    DCP_LDS char* stage = ring + (t % kStages) * P::kStageB;
+    if (n == P::kPerWave - 1 && ii >= P::kInst) {
+      if constexpr (FP8) {
+        // The scale copy: 32 token scales, lanes 32-63 repeat lanes 0-31.
+        if (cw == P::kCodeHi) {
+          const int row = lane & 31;
+          const char* src = row < sr.nvalid ? sr.sbase + 4 * row : a.zero;
+          __builtin_amdgcn_global_load_lds(src, stage + P::kScaleOff, 4, 0, kCopyPolicy);
+        }
+      }
+      return;
+    }
     // (Operands bound to locals: with the expressions inline in the
     // builtin's argument list the host pass drops this kernel's stub.)
     const char* src = cp_row[n] < sr.nvalid ? sr.base + cp_off[n] : a.zero;
-    DCP_LDS char* ldst = ring + (t % kStages) * kTileB + ii * 1024;
+    DCP_LDS char* ldst = stage + ii * 1024;
     __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, kCopyPolicy);
   };
 
@@ -915,28 +1033,38 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   auto run = [&](auto role) {
     constexpr bool kScorer = decltype(role)::value;
     // Score waves: the 18 query fragments of head head0 + 16grp + l16 of
-    // sequence qb (B operand of S^T, columns 32kk + 8q4 .. +7). Value waves:
-    // O^T accumulators, M tile mt and head tile nt at 4mt + nt.
-    constexpr int kSt = kScorer ? kKSteps : 4 * PP::kMT;
+    // sequence qb (B operand of S^T, K step kk; fp16 for an fp8 cache). Value
+    // waves: O^T accumulators, M tile mt and head tile nt at 4mt + nt.
+    constexpr int kSt = kScorer ? kKSteps : 4 * P::kMT;
     f32x4 st[kSt];
 #pragma unroll
     for (int i = 0; i < kSt; ++i) st[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     int qb = -1;
     auto load_q = [&](int b) {
+      // K step kk covers query columns 32kk + 8q4 .. +7 (bf16), or
+      // 64(kk / 2) + 16q4 + 8(kk % 2) .. +7 (fp8, the chunk order above).
       const uint16_t* qrow =
-          a.q + (static_cast<size_t>(b) * a.Hq + head0 + 16 * grp + l16) * kQK + 8 * q4;
+          a.q + (static_cast<size_t>(b) * a.Hq + head0 + 16 * grp + l16) * kQK + (FP8 ? 16 : 8) * q4;
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk)
-        st[kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + 32 * kk));
+      for (int kk = 0; kk < kKSteps; ++kk) {
+        const int col = FP8 ? 64 * (kk >> 1) + 8 * (kk & 1) : 32 * kk;
+        st[kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + col));
+      }
       // Consume the loads here, in order: the compiler then waits for exactly
       // these loads (and what was issued before them), instead of placing a
       // wait for every outstanding copy in front of each later use.
 #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk) asm volatile("" : "+v"(st[kk]));
+      if constexpr (FP8) {
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk)
+          st[kk] = __builtin_bit_cast(f32x4, E::from_bf16(__builtin_bit_cast(bf16x8, st[kk])));
+      }
       qb = b;
     };
     float m_ref = -INFINITY;  // score waves: reference max (log2 units) of head 16grp + l16
     float l_run = 0.f;        // score waves: this lane's probability sum for that head
+    float l_rnd = 0.f;        // bf16: the same sum over the probabilities as rounded for P^T
     int nfin = 0;             // segments finished so far (parity selects the fin buffer)
 
     int wpos = range0;
@@ -951,12 +1079,12 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           hi = a.seg_off[sl + 1];
         }
         int wend = end;
-        if (s_cur + PP::kMaxPieces <= a.S)
-          wend = min(wend, __shfl(hi, PP::kMaxPieces - 1));  // start of segment s_cur + 32
-        wend = min(wend, wpos + PP::kMaxTiles / (bs / kT));
+        if (s_cur + P::kMaxPieces <= a.S)
+          wend = min(wend, __shfl(hi, P::kMaxPieces - 1));  // start of segment s_cur + 32
+        wend = min(wend, wpos + P::kMaxTiles / (bs / kT));
         const int pstart = max(lo, wpos);
         const int pend = min(hi, wend);
-        const int nblk = (lane < PP::kMaxPieces && sl < a.S) ? max(0, pend - pstart) : 0;
+        const int nblk = (lane < P::kMaxPieces && sl < a.S) ? max(0, pend - pstart) : 0;
         int ntok = 0, b = 0, i0 = 0;
         if (nblk > 0) {
           b = sl / D;
@@ -976,27 +1104,27 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         const int T = __shfl(ts, 63);
         ts -= ntiles;
         const int flags = (pstart == max(lo, range0) ? 1 : 0) | (pend == min(hi, end) ? 2 : 0);
-        if (lane < PP::kMaxPieces) {
-          *reinterpret_cast<DCP_LDS i32x4*>(aux + PP::kPieceOff + 32 * lane) = i32x4{sl, b, i0, 0};
-          *reinterpret_cast<DCP_LDS i32x4*>(aux + PP::kPieceOff + 32 * lane + 16) =
+        if (lane < P::kMaxPieces) {
+          *reinterpret_cast<DCP_LDS i32x4*>(aux + P::kPieceOff + 32 * lane) = i32x4{sl, b, i0, 0};
+          *reinterpret_cast<DCP_LDS i32x4*>(aux + P::kPieceOff + 32 * lane + 16) =
               i32x4{ts, ntiles, ntok, flags};
         }
-        if (lane == 0) *reinterpret_cast<DCP_LDS i32x4*>(aux + PP::kMiscOff) = i32x4{T, wend, 0, 0};
+        if (lane == 0) *reinterpret_cast<DCP_LDS i32x4*>(aux + P::kMiscOff) = i32x4{T, wend, 0, 0};
       }
       __syncthreads();
-      const i32x4 misc = *reinterpret_cast<const DCP_LDS i32x4*>(aux + PP::kMiscOff);
+      const i32x4 misc = *reinterpret_cast<const DCP_LDS i32x4*>(aux + P::kMiscOff);
       const int T = misc[0];
       const int wend = misc[1];
       for (int t = threadIdx.x; t < T; t += 512) {
         // piece p: last piece whose first tile is <= t (a piece without tiles
         // shares its first tile with the next one, which is found instead)
         int p = 0;
-        for (int step = PP::kMaxPieces / 2; step > 0; step >>= 1) {
-          const int ts = *reinterpret_cast<const DCP_LDS int*>(aux + PP::kPieceOff + 32 * (p + step) + 16);
+        for (int step = P::kMaxPieces / 2; step > 0; step >>= 1) {
+          const int ts = *reinterpret_cast<const DCP_LDS int*>(aux + P::kPieceOff + 32 * (p + step) + 16);
           if (ts <= t) p += step;
         }
-        const i32x4 pa = *reinterpret_cast<const DCP_LDS i32x4*>(aux + PP::kPieceOff + 32 * p);
-        const i32x4 pb = *reinterpret_cast<const DCP_LDS i32x4*>(aux + PP::kPieceOff + 32 * p + 16);
+        const i32x4 pa = *reinterpret_cast<const DCP_LDS i32x4*>(aux + P::kPieceOff + 32 * p);
+        const i32x4 pb = *reinterpret_cast<const DCP_LDS i32x4*>(aux + P::kPieceOff + 32 * p + 16);
         const int j = t - pb[0];
         const int tok = j * kT;
         const int b = pa[1];
@@ -1008,23 +1136,23 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
                            (static_cast<unsigned>(p) << 16) |
                            ((j == 0 && (pb[3] & 1)) ? (1u << 30) : 0u) |
                            ((j == pb[1] - 1 && (pb[3] & 2)) ? (1u << 31) : 0u);
-        *reinterpret_cast<DCP_LDS i32x2*>(aux + PP::kTileOff + 8 * t) = i32x2{id, static_cast<int>(y)};
+        *reinterpret_cast<DCP_LDS i32x2*>(aux + P::kTileOff + 8 * t) = i32x2{id, static_cast<int>(y)};
       }
       wait_vm<0>();
       __syncthreads();
-      // prologue: tiles 0 and 1
-      for (int t = 0; t < 2 && t < T; ++t) {
+      // prologue: the first kAhead tiles
+      for (int t = 0; t < kAhead && t < T; ++t) {
         const Src sr = tile_src(tile_info(t));
-        static_for<0, PP::kPerWave>([&](auto nc) { copy_one(nc, sr, t); });
+        static_for<0, P::kPerWave>([&](auto nc) { copy_one(nc, sr, t); });
       }
 
       // Start of step ks (score waves on tile ks, value waves on tile ks - 1):
       // this wave's copies of tile ks have landed, then the barrier makes every
       // wave's copies visible and guarantees that step ks - 1 is finished, so
-      // the stage of tile ks - 2 is free for tile ks + 2. Both roles pass the
-      // same barriers in the same order.
+      // the stage of tile ks - 2 is free for tile ks + kAhead. Both roles pass
+      // the same barriers in the same order.
       auto step_begin = [&](int ks) {
-        if (ks < T) wait_tiles(ks + 1 < T ? 1 : 0);
+        if (ks < T) wait_tiles(min(kAhead - 1, T - 1 - ks));
         lds_barrier();
       };
 
@@ -1032,68 +1160,98 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         i32x2 e_cur = {0, 0}, e_iss = {0, 0};
         if (T > 0) {
           entry_read(e_cur, 0);
-          entry_read(e_iss, min(2, T - 1));
+          entry_read(e_iss, min(kAhead, T - 1));
         }
         for (int ks = 0; ks < T; ++ks) {
           step_begin(ks);
           const TileInfo ti = entry_take(e_cur);
           const TileInfo tiss = entry_take(e_iss);
           entry_read(e_cur, min(ks + 1, T - 1));
-          entry_read(e_iss, min(ks + 3, T - 1));
+          entry_read(e_iss, min(ks + 1 + kAhead, T - 1));
           if (ti.first()) {
             m_ref = -INFINITY;
             l_run = 0.f;
+            l_rnd = 0.f;
             // A new sequence needs its query. (Loaded here, in the iteration
             // that uses it, the compiler's waits for it are exact and do not
             // drain the copies in flight.)
             const int b = piece_b(ti.piece());
             if (b != qb) load_q(b);
           }
-          const bool do_issue = ks + 2 < T;
-          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, 0};
-          const uint32_t tile = ring_addr + (ks % kStages) * kTileB;
-          i32x4 ra[PP::kSRing], rb[PP::kSRing];
+          const bool do_issue = ks + kAhead < T;
+          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, a.kv_scale, 0};
+          const uint32_t tile = ring_addr + (ks % kStages) * P::kStageB;
+          // fp8: the token scales of this lane's score rows 4q4 + i and 16 + 4q4 + i
+          i32x4 sc0 = {0, 0, 0, 0}, sc1 = {0, 0, 0, 0};
+          if constexpr (FP8) {
+            lds_b128<0>(sc0, tile + P::kScaleOff + 16 * q4);
+            lds_b128<64>(sc1, tile + P::kScaleOff + 16 * q4);
+          }
+          i32x4 ra[P::kSRing], rb[P::kSRing];
           auto s_issue = [&](auto kc) {
             constexpr int kk = decltype(kc)::value;
-            constexpr int off = 128 * (kk >> 1);
-            if constexpr (kk & 1) {
-              lds_b128<off>(ra[kk % PP::kSRing], tile + a0o);
-              lds_b128<off>(rb[kk % PP::kSRing], tile + a1o);
+            constexpr int off = FP8 ? 64 * kk : 128 * (kk >> 1);
+            if constexpr (!FP8 && (kk & 1)) {
+              lds_b128<off>(ra[kk % P::kSRing], tile + a0o);
+              lds_b128<off>(rb[kk % P::kSRing], tile + a1o);
             } else {
-              lds_b128<off>(ra[kk % PP::kSRing], tile + a0e);
-              lds_b128<off>(rb[kk % PP::kSRing], tile + a1e);
+              lds_b128<off>(ra[kk % P::kSRing], tile + a0e);
+              lds_b128<off>(rb[kk % P::kSRing], tile + a1e);
             }
           };
-          static_for<0, PP::kSDist>(s_issue);
+          static_for<0, P::kSDist>(s_issue);
           f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
-          static_for<0, kKSteps>([&](auto kc) {
+          static_for<0, P::kSteps>([&](auto kc) {
             constexpr int kk = decltype(kc)::value;
-            if constexpr (kk + PP::kSDist < kKSteps) s_issue(IC<kk + PP::kSDist>{});
-            constexpr int ahead = kk + PP::kSDist < kKSteps ? PP::kSDist : kKSteps - 1 - kk;
-            wait_lgkm<2 * ahead>(ra[kk % PP::kSRing], rb[kk % PP::kSRing]);
-            const bf16x8 qv = __builtin_bit_cast(bf16x8, st[kk]);
-            if constexpr (kk & 1) {
-              s0b = E::mfma(ra[kk % PP::kSRing], qv, s0b);
-              s1b = E::mfma(rb[kk % PP::kSRing], qv, s1b);
+            if constexpr (kk + P::kSDist < P::kSteps) s_issue(IC<kk + P::kSDist>{});
+            constexpr int ahead = kk + P::kSDist < P::kSteps ? P::kSDist : P::kSteps - 1 - kk;
+            wait_lgkm<2 * ahead>(ra[kk % P::kSRing], rb[kk % P::kSRing]);
+            if constexpr (FP8) {
+              // read kk: K steps 2kk (codes 0-7) and 2kk + 1 (codes 8-15)
+              const i32x4 ua = ra[kk % P::kSRing], ub = rb[kk % P::kSRing];
+              const i32x4 a00 = f8x8_to_f16x8(ua[0], ua[1]), a01 = f8x8_to_f16x8(ua[2], ua[3]);
+              const i32x4 a10 = f8x8_to_f16x8(ub[0], ub[1]), a11 = f8x8_to_f16x8(ub[2], ub[3]);
+              const f16x8 q0 = __builtin_bit_cast(f16x8, st[2 * kk]);
+              const f16x8 q1 = __builtin_bit_cast(f16x8, st[2 * kk + 1]);
+              s0a = E::mfma(a00, q0, s0a);
+              s1a = E::mfma(a10, q0, s1a);
+              s0b = E::mfma(a01, q1, s0b);
+              s1b = E::mfma(a11, q1, s1b);
             } else {
-              s0a = E::mfma(ra[kk % PP::kSRing], qv, s0a);
-              s1a = E::mfma(rb[kk % PP::kSRing], qv, s1a);
+              const bf16x8 qv = __builtin_bit_cast(bf16x8, st[kk]);
+              if constexpr (kk & 1) {
+                s0b = E::mfma(ra[kk % P::kSRing], qv, s0b);
+                s1b = E::mfma(rb[kk % P::kSRing], qv, s1b);
+              } else {
+                s0a = E::mfma(ra[kk % P::kSRing], qv, s0a);
+                s1a = E::mfma(rb[kk % P::kSRing], qv, s1a);
+              }
             }
-            // copies n in [n0, n1) go out after this K step
-            constexpr int n0 = kk < PP::kSSpread ? kk * PP::kPerWave / PP::kSSpread : PP::kPerWave;
-            constexpr int n1 = kk < PP::kSSpread ? (kk + 1) * PP::kPerWave / PP::kSSpread : PP::kPerWave;
-            if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + 2); });
+            // copies n in [n0, n1) go out after this read
+            constexpr int n0 = kk < P::kSSpread ? kk * P::kPerWave / P::kSSpread : P::kPerWave;
+            constexpr int n1 = kk < P::kSSpread ? (kk + 1) * P::kPerWave / P::kSSpread : P::kPerWave;
+            if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
           });
           const f32x4 sv0 = s0a + s0b, sv1 = s1a + s1b;
 
           // Online softmax of head 16grp + l16 over this lane's 8 tokens
           // (4q4 + i and 16 + 4q4 + i), exp2 domain.
           const unsigned vm = ti.rows();
-          float x[8];
+          float x[8], sig[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             x[i] = sv0[i] * a.scale_log2;
             x[4 + i] = sv1[i] * a.scale_log2;
+          }
+          if constexpr (FP8) {
+            wait_lgkm<0>(sc0, sc1);  // (arrived before the last fragments)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              sig[i] = __int_as_float(sc0[i]);
+              sig[4 + i] = __int_as_float(sc1[i]);
+              x[i] *= sig[i];
+              x[4 + i] *= sig[4 + i];
+            }
           }
           if (vm != 0xffffffffu) {  // a tile with rows past the end (wave-uniform)
             const unsigned lo = vm >> (4 * q4), hi = vm >> (16 + 4 * q4);
@@ -1107,8 +1265,8 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
                              fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
           hmax = max_xor32(max_xor16(hmax));
           // The reference only rises when the tile's max exceeds it by more
-          // than 8, so probabilities stay <= 256 and rescales are rare.
-          const bool raise = hmax > m_ref + 8.f;
+          // than kRaise, so probabilities stay <= 2^kRaise and rescales are rare.
+          const bool raise = hmax > m_ref + P::kRaise;
           const float alpha = raise ? fast_exp2(m_ref - hmax) : 1.f;  // 0 when m_ref = -inf
           m_ref = raise ? hmax : m_ref;
           const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
@@ -1117,20 +1275,28 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(x[i] - m_use);
           l_run = l_run * alpha +
                   (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+          if constexpr (FP8) {
+            // the value waves weight each token's codes by p * scale
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pr[i] *= sig[i];
+          }
           const i32x4 pk = {static_cast<int>(E::pack2(pr[0], pr[1])),
                             static_cast<int>(E::pack2(pr[2], pr[3])),
                             static_cast<int>(E::pack2(pr[4], pr[5])),
                             static_cast<int>(E::pack2(pr[6], pr[7]))};
-          lds_store_b128(aux_addr + PP::kPOff + (ks & 1) * PP::kPBufB + (grp * 64 + lane) * 16, pk);
+          if constexpr (!FP8) l_rnd = add_bf16x8(pk, l_rnd * alpha);
+          lds_store_b128(aux_addr + P::kPOff + (ks & 1) * P::kPBufB + (grp * 64 + lane) * 16, pk);
           const bool any = __ballot(raise) != 0ull;
           if (lane == 0) lds_store_b8(flags_addr + (ks & 1) * 4 + grp, any ? 1 : 0);
           if (any && q4 == 0)
-            lds_store_b32(aux_addr + PP::kAlphaOff + (((ks & 1) * 16 + l16) * 4 + grp) * 4, alpha);
+            lds_store_b32(aux_addr + P::kAlphaOff + (((ks & 1) * 16 + l16) * 4 + grp) * 4, alpha);
           if (ti.last()) {
-            // Segment done: its head sums for the value waves, and its LSE.
+            // Segment done: its head sums for the value waves (bf16: of the
+            // rounded probabilities), and its LSE.
             const float l_h = sum_xor32(sum_xor16(l_run));
+            const float l_o = FP8 ? l_h : sum_xor32(sum_xor16(l_rnd));
             if (q4 == 0) {
-              lds_store_b32(aux_addr + PP::kFinOff + ((nfin & 1) * 64 + 16 * grp + l16) * 4, l_h);
+              lds_store_b32(aux_addr + P::kFinOff + ((nfin & 1) * 64 + 16 * grp + l16) * 4, l_o);
               const size_t slot = static_cast<size_t>(piece_s(ti.piece())) + g;
               a.ws_lse[slot * a.Hq + head0 + 16 * grp + l16] =
                   l_h > 0.f ? (m_ref + fast_log2(l_h)) * kLn2 : -INFINITY;
@@ -1140,25 +1306,25 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         }
         step_begin(T);  // the value waves' last step
       } else {
-        // Step 0 has no value tile yet: only this wave's copies of tile 2.
+        // Step 0 has no value tile yet: only this wave's copies of tile kAhead.
         step_begin(0);
-        if (2 < T) {
-          const Src nsrc = tile_src(tile_info(2));
-          static_for<0, PP::kPerWave>([&](auto nc) { copy_one(nc, nsrc, 2); });
+        if (kAhead < T) {
+          const Src nsrc = tile_src(tile_info(kAhead));
+          static_for<0, P::kPerWave>([&](auto nc) { copy_one(nc, nsrc, kAhead); });
         }
         i32x2 e_kv = {0, 0}, e_iss = {0, 0};
         if (T > 0) {
           entry_read(e_kv, 0);
-          entry_read(e_iss, min(3, T - 1));
+          entry_read(e_iss, min(1 + kAhead, T - 1));
         }
         for (int ks = 1; ks <= T; ++ks) {
           step_begin(ks);
           const TileInfo ti = entry_take(e_kv);
           const TileInfo tiss = entry_take(e_iss);
           entry_read(e_kv, min(ks, T - 1));
-          entry_read(e_iss, min(ks + 3, T - 1));
-          const bool do_issue = ks + 2 < T;
-          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, 0};
+          entry_read(e_iss, min(ks + 1 + kAhead, T - 1));
+          const bool do_issue = ks + kAhead < T;
+          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, a.kv_scale, 0};
           const int kv = ks - 1;
           // LDS reads of this step, oldest first: the rescale votes of tile kv,
           // its P^T fragments, then the first transposed tile fragments; the
@@ -1166,58 +1332,69 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           int fl;
           lds_b32<0>(fl, flags_addr + (kv & 1) * 4);
           i32x4 pb[4];
-          const uint32_t pbase = aux_addr + PP::kPOff + (kv & 1) * PP::kPBufB + lane * 16;
+          const uint32_t pbase = aux_addr + P::kPOff + (kv & 1) * P::kPBufB + lane * 16;
           static_for<0, 4>([&](auto nc) {
             constexpr int nt = decltype(nc)::value;
             lds_b128<nt * 1024>(pb[nt], pbase);
           });
-          const uint32_t tile = ring_addr + (kv % kStages) * kTileB;
-          uint32_t tb[8];
+          const uint32_t tile = ring_addr + (kv % kStages) * P::kStageB;
+          uint32_t tb[kTOff];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) tb[j] = tile + t_off[j];
-          i32x2 rlo[PP::kPD + 2], rhi[PP::kPD + 2];
+          for (int j = 0; j < kTOff; ++j) tb[j] = tile + t_off[j];
+          constexpr int kVRing = P::kPD < P::kMT ? P::kPD + 2 : P::kMT;
+          i32x2 rlo[kVRing], rhi[kVRing];
           auto p_issue = [&](auto mc) {
             constexpr int mt = decltype(mc)::value;
-            constexpr int off = 128 * (mt >> 2);
-            lds_tr<off>(rlo[mt % (PP::kPD + 2)], tb[mt & 3]);
-            lds_tr<off>(rhi[mt % (PP::kPD + 2)], tb[4 + (mt & 3)]);
+            if constexpr (FP8) {
+              lds_tr8<64 * (mt >> 2)>(rlo[mt % kVRing], tb[mt & 3]);
+            } else {
+              constexpr int off = 128 * (mt >> 2);
+              lds_tr<off>(rlo[mt % kVRing], tb[mt & 3]);
+              lds_tr<off>(rhi[mt % kVRing], tb[4 + (mt & 3)]);
+            }
           };
-          static_for<0, PP::kPD>(p_issue);
-          wait_lgkm<4 + 2 * PP::kPD>(fl);  // (at most 15 LDS reads are ever outstanding)
+          static_for<0, P::kPD>(p_issue);
+          wait_lgkm<4 + P::kPReads * P::kPD>(fl);  // (at most 15 LDS reads are ever outstanding)
           const int fb = wave_uniform(fl);
           if (fb != 0) {
             // Rescale factors of heads whose reference max rose in tile kv.
             i32x4 al;
-            lds_b128<0>(al, aux_addr + PP::kAlphaOff + ((kv & 1) * 16 + l16) * 16);
+            lds_b128<0>(al, aux_addr + P::kAlphaOff + ((kv & 1) * 16 + l16) * 16);
             wait_lgkm<0>(al);
             const f32x4 alv = __builtin_bit_cast(f32x4, al);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
               if ((fb >> (8 * nt)) & 0xff)
 #pragma unroll
-                for (int mt = 0; mt < PP::kMT; ++mt) st[4 * mt + nt] *= alv[nt];
+                for (int mt = 0; mt < P::kMT; ++mt) st[4 * mt + nt] *= alv[nt];
           }
-          static_for<0, PP::kMT>([&](auto mc) {
+          static_for<0, P::kMT>([&](auto mc) {
             constexpr int mt = decltype(mc)::value;
-            if constexpr (mt + PP::kPD < PP::kMT) p_issue(IC<mt + PP::kPD>{});
-            constexpr int ahead = mt + PP::kPD < PP::kMT ? PP::kPD : PP::kMT - 1 - mt;
-            wait_lgkm<2 * ahead>(rlo[mt % (PP::kPD + 2)], rhi[mt % (PP::kPD + 2)]);
-            const i32x4 av = {rlo[mt % (PP::kPD + 2)][0], rlo[mt % (PP::kPD + 2)][1],
-                              rhi[mt % (PP::kPD + 2)][0], rhi[mt % (PP::kPD + 2)][1]};
+            if constexpr (mt + P::kPD < P::kMT) p_issue(IC<mt + P::kPD>{});
+            constexpr int ahead = mt + P::kPD < P::kMT ? P::kPD : P::kMT - 1 - mt;
+            i32x4 av;
+            if constexpr (FP8) {
+              wait_lgkm<ahead>(rlo[mt % kVRing]);
+              av = f8x8_to_f16x8(rlo[mt % kVRing][0], rlo[mt % kVRing][1]);
+            } else {
+              wait_lgkm<2 * ahead>(rlo[mt % kVRing], rhi[mt % kVRing]);
+              av = i32x4{rlo[mt % kVRing][0], rlo[mt % kVRing][1], rhi[mt % kVRing][0],
+                         rhi[mt % kVRing][1]};
+            }
             static_for<0, 4>([&](auto nc) {
               constexpr int nt = decltype(nc)::value;
-              st[4 * mt + nt] = E::mfma(av, __builtin_bit_cast(bf16x8, pb[nt]), st[4 * mt + nt]);
+              st[4 * mt + nt] = E::mfma(av, __builtin_bit_cast(typename E::vec, pb[nt]), st[4 * mt + nt]);
             });
-            constexpr int n0 = mt < PP::kVSpread ? mt * PP::kPerWave / PP::kVSpread : PP::kPerWave;
-            constexpr int n1 = mt < PP::kVSpread ? (mt + 1) * PP::kPerWave / PP::kVSpread : PP::kPerWave;
-            if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + 2); });
+            constexpr int n0 = mt < P::kVSpread ? mt * P::kPerWave / P::kVSpread : P::kPerWave;
+            constexpr int n1 = mt < P::kVSpread ? (mt + 1) * P::kPerWave / P::kVSpread : P::kPerWave;
+            if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
           });
           if (ti.last()) {
             // Segment done: normalise by the score waves' head sums and store
             // (O, slot s + g); the accumulators restart at zero.
             const size_t slot = static_cast<size_t>(piece_s(ti.piece())) + g;
             // fin[16nt + l16] for nt = 0..3
-            const uint32_t fa = aux_addr + PP::kFinOff + ((nfin & 1) * 64 + l16) * 4;
+            const uint32_t fa = aux_addr + P::kFinOff + ((nfin & 1) * 64 + l16) * 4;
             int l0, l1, l2, l3;
             lds_b32<0>(l0, fa);
             lds_b32<64>(l1, fa);
@@ -1232,7 +1409,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
               const float inv = lt[nt] > 0.f ? 1.f / lt[nt] : 0.f;
               float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
 #pragma unroll
-              for (int mt = 0; mt < PP::kMT; ++mt) {
+              for (int mt = 0; mt < P::kMT; ++mt) {
                 *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
                 st[4 * mt + nt] = f32x4{0.f, 0.f, 0.f, 0.f};
               }
@@ -1296,8 +1473,9 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   const bool bs32 = d->block_size % kT == 0 && a.token_stride_b * kT < (1ll << 30);
   const int heads = d->num_q_heads < 64 ? d->num_q_heads : 64;
   const dim3 grid(kGroups, d->num_q_heads / heads);
-  if (!fp8 && bs32 && heads == 64) {
-    hipLaunchKernelGGL(mla_pp_kernel, grid, dim3(512), 0, stream, a);
+  if (bs32 && heads == 64) {
+    if (fp8) hipLaunchKernelGGL(mla_pp_kernel<true>, grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL(mla_pp_kernel<false>, grid, dim3(512), 0, stream, a);
     return hipGetLastError();
   }
   switch (heads / 16) {

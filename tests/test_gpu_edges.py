@@ -21,6 +21,8 @@ CASES = [
     ("mla", "bf16", 128, 2, 128, 1, 576),
     ("mla", "bf16", 1, 8, 16, 1, 576),
     ("mla", "fp8", 48, 5, 64, 1, 576),
+    ("mla", "fp8", 32, 3, 64, 1, 576),
+    ("mla", "fp8", 128, 2, 128, 1, 576),
     ("gqa", "bf16", 16, 4, 64, 8, 128),
     ("gqa", "bf16", 16, 3, 16, 1, 64),
     ("gqa", "bf16", 8, 2, 32, 2, 128),
@@ -78,3 +80,21 @@ def test_unusable_block_ids_are_skipped(kind, dtype):
         o_ref[b], lse_ref[b] = oracle.attend(oracle.query(w, b), k, v, w.spec.softmax_scale)
     o, lse, _, _ = run_all_shards(w)
     compare(o, lse, o_ref, lse_ref, **TOL[dtype], label="skipped ids")
+
+
+@pytest.mark.parametrize("kind,dtype,bs,hq,hkv,dim", [
+    ("mla", "bf16", 64, 64, 1, 576),
+    ("mla", "fp8", 64, 64, 1, 576),
+    ("mla", "fp8", 64, 32, 1, 576),
+    ("gqa", "bf16", 16, 64, 8, 128),
+])
+def test_sharp_softmax(kind, dtype, bs, hq, hkv, dim):
+    """A large softmax scale spreads the scores over tens of log2 units, so a
+    head's running maximum rises (and its accumulators are rescaled) many
+    times within a shard's range, and most probabilities underflow."""
+    w = W.custom(kind, [3000, 777, 4096], num_q_heads=hq, num_kv_heads=hkv, qk_dim=dim,
+                 v_dim=512 if kind == "mla" else dim, block_size=bs, num_shards=4,
+                 kv_dtype=dtype, softmax_scale=0.5, seed=5)
+    o_ref, lse_ref = oracle.decode_reference(w)
+    o, lse, _, _ = run_all_shards(w)
+    compare(o, lse, o_ref, lse_ref, **TOL[dtype], label="sharp softmax")

@@ -78,7 +78,9 @@ dcp_status_t run_attention(const dcp_attn_desc_t* d, const void* q, const void* 
   WorkspaceView ws = carve_workspace(workspace, S, G, d->batch, d->num_q_heads, d->v_dim);
   // Fixed work per piece of a segment, in blocks (about 128 tokens' worth).
   const int seg_cost = (128 + d->block_size - 1) / d->block_size;
-  if (launch_plan(m, S, G, seg_cost, d->num_q_heads, ws, stream) != hipSuccess) return DCP_ERR_HIP;
+  const bool seq_pieces = d->kv_kind == DCP_KV_LATENT && mla_sequence_pieces(d);
+  if (launch_plan(m, S, G, seg_cost, d->num_q_heads, seq_pieces, ws, stream) != hipSuccess)
+    return DCP_ERR_HIP;
   AttnLaunch L{d, q, k, v, kv_scale, m, S, ws};
   if (attn_begin && hipEventRecord(attn_begin, stream) != hipSuccess) return DCP_ERR_HIP;
   hipError_t err = d->kv_kind == DCP_KV_LATENT ? launch_mla(L, stream) : launch_gqa(L, stream);

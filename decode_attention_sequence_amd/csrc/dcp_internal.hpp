@@ -188,8 +188,8 @@ struct WorkspaceView {
 size_t workspace_bytes_for(int S, int G, int B, int Hq, int v_dim);
 WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim);
 
-hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, int Hq, WorkspaceView ws,
-                       hipStream_t stream);
+hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, int Hq, bool seq_pieces,
+                       WorkspaceView ws, hipStream_t stream);
 hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, int G, int Hq, int v_dim,
                                void* out, dcp_dtype_t out_dtype, float* lse_out,
                                hipStream_t stream);
@@ -215,6 +215,9 @@ struct AttnLaunch {
 int mla_groups();
 int gqa_groups(const dcp_attn_desc_t* desc);
 bool mla_supported(const dcp_attn_desc_t* desc);
+// True when the MLA kernel for desc keeps one partial per work group and
+// sequence (slot b + g) rather than one per work group and segment (slot s + g).
+bool mla_sequence_pieces(const dcp_attn_desc_t* desc);
 bool gqa_supported(const dcp_attn_desc_t* desc);
 hipError_t launch_mla(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_gqa(const AttnLaunch& a, hipStream_t stream);

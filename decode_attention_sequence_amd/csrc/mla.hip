@@ -756,6 +756,15 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
 //    tile table in LDS, and segment boundaries inside a window are handled
 //    per tile (state reset, query reload, result store) without draining the
 //    copy pipeline.
+//  * fp8 cache: the score waves are pipelined one tile deeper -- during step
+//    t they compute S^T of tile t and, interleaved with those MFMAs, the
+//    softmax of tile t - 1 (whose scores they kept in registers); the value
+//    waves work on tile t - 2. The softmax latency then overlaps the score
+//    MFMAs instead of following them. Seven ring stages keep four tiles in
+//    flight; every wave issues the same three 16-byte copies per tile (code
+//    rows, the token scales, or a filler into a pad), also past the end of a
+//    window, so the copy loops have no branches and the copy waits are
+//    constant.
 //  * fp8 cache: each tile carries its 32 token scales. The codes are widened
 //    to fp16 in registers right after each LDS fragment read (exact; see
 //    f8x8_to_f16x8) and both products run on v_mfma_f32_16x16x32_f16. A score
@@ -769,16 +778,20 @@ struct PP {
   static constexpr int kRowBytes = FP8 ? kF8RowB : kRowB;    // cache row bytes in LDS
   static constexpr int kCodeB = FP8 ? kF8TileB : kTileB;     // tile bytes without scales
   static constexpr int kInst = FP8 ? kF8DmaInst : kDmaInst;  // wave-wide 16-byte copies per tile
+  static constexpr bool kPipe = FP8;                         // softmax one tile behind the scores
   static constexpr int kScaleOff = kCodeB;                   // fp8: token scales of the tile
-  static constexpr int kStageB = FP8 ? kCodeB + 256 : kCodeB;
-  static constexpr int kStages = FP8 ? 6 : 4;                // ring stages
-  static constexpr int kAhead = kStages - 2;                 // tiles copied ahead of the scores
+  static constexpr int kScaleB = FP8 ? 1024 : 0;             // (one wave-wide copy; 128 B used)
+  static constexpr int kStageB = kCodeB + kScaleB;
+  static constexpr int kStages = FP8 ? 7 : 4;                // ring stages
+  static constexpr int kAhead = kStages - (kPipe ? 3 : 2);   // tiles copied ahead of the scores
   static constexpr int kMT = 8;                              // 16-column M tiles per value wave
   static constexpr int kPerWave = (kInst + 7) / 8;           // copy rounds per tile (at most)
   // Copy groups cw < kCodeHi issue kPerWave code copies per tile, the others
-  // one fewer; for fp8 group kCodeHi also copies the tile's token scales.
+  // one fewer (bf16). fp8: group kCodeHi copies the token scales instead and
+  // the remaining groups a filler, so every wave issues kPerWave copies.
   static constexpr int kCodeHi = kInst % 8 ? kInst % 8 : 8;
-  static constexpr int kHiWaves = FP8 ? kCodeHi + 1 : kCodeHi;  // groups with kPerWave operations
+  static constexpr int kHiWaves = FP8 ? 8 : kCodeHi;         // groups with kPerWave operations
+  static constexpr int kSmAt = 2;                            // fp8: softmax after this score read
   static constexpr int kSteps = FP8 ? kKSteps / 2 : kKSteps;    // score fragment reads per M tile
   static constexpr int kSDist = 3;                           // score reads in flight (per M tile)
   static constexpr int kSRing = kSDist + 2;
@@ -797,7 +810,8 @@ struct PP {
   static constexpr float kRaise = FP8 ? 4.f : 8.f;
   static constexpr int kMaxPieces = 32;                      // segments per window
   static constexpr int kMaxTiles = 640;                      // tiles per window
-  static constexpr int kRingB = kStages * kStageB;
+  static constexpr int kPadOff = kStages * kStageB;          // fp8: landing pad of the fillers
+  static constexpr int kRingB = kPadOff + (FP8 ? 1024 : 0);
   static constexpr int kPBufB = 4 * 64 * 16;                 // P^T of one tile, 4 head groups
   static constexpr int kPOff = 0;                            // [2] tiles
   static constexpr int kAlphaOff = kPOff + 2 * kPBufB;       // [2][16 lanes][4 groups] floats
@@ -811,8 +825,9 @@ struct PP {
 };
 // Tile table entry: x = block id (-1: unusable, the tile's rows read zeros),
 // y = tile offset in the block / 32 (bits 0-7), valid rows - 1 (bits 8-15),
-// piece (bits 16-23), first tile of its segment (bit 30), last tile of its
-// segment (bit 31).
+// piece (bits 16-23), first tile of its sequence in the work group's range
+// (bit 30), last such tile (bit 31). The sequence's partial of this range goes
+// to slot b + g.
 // Piece entry: {s, b, first local block, -}, {first tile, tiles, tokens, -}.
 
 __device__ __forceinline__ void lds_store_b32(uint32_t addr, float v) {
@@ -978,12 +993,6 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
     wait_lgkm<0>(e);
     return TileInfo{wave_uniform(e[0]), wave_uniform(e[1])};
   };
-  auto piece_s = [&](int p) -> int {  // segment of piece p
-    int v;
-    lds_b32<0>(v, piece_addr + 32 * p);
-    wait_lgkm<0>(v);
-    return wave_uniform(v);
-  };
   auto piece_b = [&](int p) -> int {  // sequence of piece p
     int v;
     lds_b32<4>(v, piece_addr + 32 * p);
@@ -1009,16 +1018,22 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
     constexpr int n = decltype(nc)::value;
     const int ii = cw + 8 * n;
     DCP_LDS char* stage = ring + (t % kStages) * P::kStageB;
-    if (n == P::kPerWave - 1 && ii >= P::kInst) {
-      if constexpr (FP8) {
-        // The scale copy: 32 token scales, lanes 32-63 repeat lanes 0-31.
-        if (cw == P::kCodeHi) {
-          const int row = lane & 31;
-          const char* src = row < sr.nvalid ? sr.sbase + 4 * row : a.zero;
-          __builtin_amdgcn_global_load_lds(src, stage + P::kScaleOff, 4, 0, kCopyPolicy);
-        }
+    if constexpr (FP8) {
+      if constexpr (n == P::kPerWave - 1) {
+        // Last round: code rows (cw < kCodeHi), the token scales (cw == kCodeHi:
+        // lanes 0-7 take four rows each; rows past nvalid lie in the same block
+        // and are masked by the scores), or a filler into the pad.
+        const bool code = cw < P::kCodeHi;
+        const bool scl = cw == P::kCodeHi;
+        const char* src = a.zero;
+        if (code && cp_row[n] < sr.nvalid) src = sr.base + cp_off[n];
+        if (scl && lane < 8 && 4 * lane < sr.nvalid) src = sr.sbase + 16 * lane;
+        DCP_LDS char* ldst = code ? stage + ii * 1024 : scl ? stage + P::kScaleOff : ring + P::kPadOff;
+        __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, kCopyPolicy);
+        return;
       }
-      return;
+    } else {
+      if (n == P::kPerWave - 1 && ii >= P::kInst) return;
     }
     // (Operands bound to locals: with the expressions inline in the
     // builtin's argument list the host pass drops this kernel's stub.)
@@ -1073,10 +1088,13 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
       // ---- window [wpos, wend): piece table (wave 0), then tile table (all)
       if (w == 0) {
         const int sl = s_cur + lane;
-        int lo = total, hi = total;
+        int lo = total, hi = total, qlo = total, qhi = total;
         if (sl < a.S) {
           lo = a.seg_off[sl];
           hi = a.seg_off[sl + 1];
+          const int s0 = sl - sl % D;  // the sequence's blocks: [seg_off[s0], seg_off[s0 + D])
+          qlo = a.seg_off[s0];
+          qhi = a.seg_off[s0 + D];
         }
         int wend = end;
         if (s_cur + P::kMaxPieces <= a.S)
@@ -1103,7 +1121,9 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         }
         const int T = __shfl(ts, 63);
         ts -= ntiles;
-        const int flags = (pstart == max(lo, range0) ? 1 : 0) | (pend == min(hi, end) ? 2 : 0);
+        // first / last piece of its sequence in this range: the accumulation
+        // runs on across the sequence's shards and ends in one partial
+        const int flags = (pstart == max(qlo, range0) ? 1 : 0) | (pend == min(qhi, end) ? 2 : 0);
         if (lane < P::kMaxPieces) {
           *reinterpret_cast<DCP_LDS i32x4*>(aux + P::kPieceOff + 32 * lane) = i32x4{sl, b, i0, 0};
           *reinterpret_cast<DCP_LDS i32x4*>(aux + P::kPieceOff + 32 * lane + 16) =
@@ -1140,9 +1160,10 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
       }
       wait_vm<0>();
       __syncthreads();
-      // prologue: the first kAhead tiles
-      for (int t = 0; t < kAhead && t < T; ++t) {
-        const Src sr = tile_src(tile_info(t));
+      // prologue: the first kAhead tiles (fp8: fillers past the last tile, so
+      // that every step is preceded by the same number of copies)
+      for (int t = 0; t < kAhead && (P::kPipe || t < T); ++t) {
+        const Src sr = t < T ? tile_src(tile_info(t)) : Src{a.kv, a.kv_scale, 0};
         static_for<0, P::kPerWave>([&](auto nc) { copy_one(nc, sr, t); });
       }
 
@@ -1152,11 +1173,253 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
       // the stage of tile ks - 2 is free for tile ks + kAhead. Both roles pass
       // the same barriers in the same order.
       auto step_begin = [&](int ks) {
-        if (ks < T) wait_tiles(min(kAhead - 1, T - 1 - ks));
+        if (ks < T) wait_tiles(P::kPipe ? kAhead - 1 : min(kAhead - 1, T - 1 - ks));
         lds_barrier();
       };
 
-      if constexpr (kScorer) {
+      if constexpr (P::kPipe) {
+       if constexpr (kScorer) {
+        i32x2 e_cur = {0, 0}, e_iss = {0, 0};
+        if (T > 0) {
+          entry_read(e_cur, 0);
+          entry_read(e_iss, min(kAhead, T - 1));
+        }
+        // Tile ks - 1, whose softmax runs in step ks: its table entry, its
+        // scores and its token scales (rows 4q4 + i and 16 + 4q4 + i).
+        TileInfo tip{-1, 0};
+        f32x4 svp0 = {0.f, 0.f, 0.f, 0.f}, svp1 = svp0;
+        i32x4 scp0 = {0, 0, 0, 0}, scp1 = scp0;
+        for (int ks = 0; ks <= T; ++ks) {
+          step_begin(ks);
+          const bool has_s = ks < T;   // step ks scores tile ks ...
+          const bool has_sm = ks > 0;  // ... and runs the softmax of tile ks - 1
+          TileInfo ti{-1, 0}, tiss{-1, 0};
+          if (has_s) {
+            ti = entry_take(e_cur);
+            tiss = entry_take(e_iss);
+            entry_read(e_cur, min(ks + 1, T - 1));
+            entry_read(e_iss, min(ks + 1 + kAhead, T - 1));
+            if (ti.first()) {
+              // A new sequence needs its query. (Loaded here, in the iteration
+              // that uses it, the compiler's waits for it are exact and do not
+              // drain the copies in flight.)
+              const int b = piece_b(ti.piece());
+              if (b != qb) load_q(b);
+            }
+          }
+          if (has_sm && tip.first()) {
+            m_ref = -INFINITY;
+            l_run = 0.f;
+          }
+          // (In the window's last step there is no tile ks: the score loop then
+          // reads a stale stage and its results are dropped; the copies are
+          // fillers.)
+          const bool do_issue = ks + kAhead < T;
+          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, a.kv_scale, 0};
+          const uint32_t tile = ring_addr + (ks % kStages) * P::kStageB;
+          i32x4 sc0, sc1;
+          lds_b128<0>(sc0, tile + P::kScaleOff + 16 * q4);
+          lds_b128<64>(sc1, tile + P::kScaleOff + 16 * q4);
+          i32x4 ra[P::kSRing], rb[P::kSRing];
+          auto s_issue = [&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            lds_b128<64 * kk>(ra[kk % P::kSRing], tile + a0e);
+            lds_b128<64 * kk>(rb[kk % P::kSRing], tile + a1e);
+          };
+          static_for<0, P::kSDist>(s_issue);
+
+          // Online softmax of tile ks - 1 for head 16grp + l16 over this lane's
+          // 8 tokens, exp2 domain. Plain arithmetic placed inside the score
+          // loop, so its latency overlaps the MFMAs; its stores follow the loop.
+          i32x4 pk = {0, 0, 0, 0};
+          float alpha = 1.f, m_new = m_ref, l_new = l_run;
+          bool raise = false;
+          auto softmax_prev = [&]() {
+            const unsigned vm = tip.rows();
+            const unsigned lo = vm >> (4 * q4), hi = vm >> (16 + 4 * q4);
+            float x[8], sig[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool v0 = (lo >> i) & 1u, v1 = (hi >> i) & 1u;
+              sig[i] = v0 ? __int_as_float(scp0[i]) : 0.f;
+              sig[4 + i] = v1 ? __int_as_float(scp1[i]) : 0.f;
+              x[i] = v0 ? svp0[i] * sig[i] * a.scale_log2 : -INFINITY;
+              x[4 + i] = v1 ? svp1[i] * sig[4 + i] * a.scale_log2 : -INFINITY;
+            }
+            float hmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                               fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+            hmax = max_xor32(max_xor16(hmax));
+            raise = hmax > m_ref + P::kRaise;
+            alpha = raise ? fast_exp2(m_ref - hmax) : 1.f;  // 0 when m_ref = -inf
+            m_new = raise ? hmax : m_ref;
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            float pr[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(x[i] - m_use);
+            l_new = l_run * alpha +
+                    (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+            // the value waves weight each token's codes by p * scale
+            pk = i32x4{static_cast<int>(E::pack2(pr[0] * sig[0], pr[1] * sig[1])),
+                       static_cast<int>(E::pack2(pr[2] * sig[2], pr[3] * sig[3])),
+                       static_cast<int>(E::pack2(pr[4] * sig[4], pr[5] * sig[5])),
+                       static_cast<int>(E::pack2(pr[6] * sig[6], pr[7] * sig[7]))};
+          };
+
+          f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
+          static_for<0, P::kSteps>([&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            if constexpr (kk + P::kSDist < P::kSteps) s_issue(IC<kk + P::kSDist>{});
+            constexpr int ahead = kk + P::kSDist < P::kSteps ? P::kSDist : P::kSteps - 1 - kk;
+            wait_lgkm<2 * ahead>(ra[kk % P::kSRing], rb[kk % P::kSRing]);
+            // read kk: K steps 2kk (codes 0-7) and 2kk + 1 (codes 8-15)
+            const i32x4 ua = ra[kk % P::kSRing], ub = rb[kk % P::kSRing];
+            const i32x4 a00 = f8x8_to_f16x8(ua[0], ua[1]), a01 = f8x8_to_f16x8(ua[2], ua[3]);
+            const i32x4 a10 = f8x8_to_f16x8(ub[0], ub[1]), a11 = f8x8_to_f16x8(ub[2], ub[3]);
+            const f16x8 q0 = __builtin_bit_cast(f16x8, st[2 * kk]);
+            const f16x8 q1 = __builtin_bit_cast(f16x8, st[2 * kk + 1]);
+            s0a = E::mfma(a00, q0, s0a);
+            s1a = E::mfma(a10, q0, s1a);
+            s0b = E::mfma(a01, q1, s0b);
+            s1b = E::mfma(a11, q1, s1b);
+            if constexpr (kk == P::kSmAt) softmax_prev();
+            // copies n in [n0, n1) go out after this read
+            constexpr int n0 = kk < P::kSSpread ? kk * P::kPerWave / P::kSSpread : P::kPerWave;
+            constexpr int n1 = kk < P::kSSpread ? (kk + 1) * P::kPerWave / P::kSSpread : P::kPerWave;
+            static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
+          });
+          const f32x4 sv0 = s0a + s0b, sv1 = s1a + s1b;
+
+          // Results of tile ks - 1. (A window's first step has none: its stores
+          // land in buffers that tile 1 rewrites before any value wave reads them.)
+          const int pp = (ks - 1) & 1;
+          lds_store_b128(aux_addr + P::kPOff + pp * P::kPBufB + (grp * 64 + lane) * 16, pk);
+          const bool any = has_sm && __ballot(raise) != 0ull;
+          if (lane == 0) lds_store_b8(flags_addr + pp * 4 + grp, any ? 1 : 0);
+          if (any && q4 == 0)
+            lds_store_b32(aux_addr + P::kAlphaOff + ((pp * 16 + l16) * 4 + grp) * 4, alpha);
+          if (has_sm) {
+            m_ref = m_new;
+            l_run = l_new;
+          }
+          if (has_sm && tip.last()) {
+            // Segment done: its head sums for the value waves, and its LSE.
+            const float l_h = sum_xor32(sum_xor16(l_run));
+            if (q4 == 0) {
+              lds_store_b32(aux_addr + P::kFinOff + ((nfin & 1) * 64 + 16 * grp + l16) * 4, l_h);
+              const size_t slot = static_cast<size_t>(piece_b(tip.piece())) + g;
+              a.ws_lse[slot * a.Hq + head0 + 16 * grp + l16] =
+                  l_h > 0.f ? (m_ref + fast_log2(l_h)) * kLn2 : -INFINITY;
+            }
+            ++nfin;
+          }
+          wait_lgkm<0>(sc0, sc1);
+          tip = ti;
+          svp0 = sv0;
+          svp1 = sv1;
+          scp0 = sc0;
+          scp1 = sc1;
+        }
+        step_begin(T + 1);  // the value waves' last step
+       } else {
+        // Steps 0 and 1 have no value tile yet: only this wave's copies. (Kept
+        // out of the loop: a loop path that leaves the accumulators untouched
+        // makes the register allocator rotate them through fresh registers.)
+        for (int ks = 0; ks < 2; ++ks) {
+          step_begin(ks);
+          const bool do_issue = ks + kAhead < T;
+          const Src nsrc = do_issue ? tile_src(tile_info(ks + kAhead)) : Src{a.kv, a.kv_scale, 0};
+          static_for<0, P::kPerWave>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
+        }
+        i32x2 e_kv = {0, 0}, e_iss = {0, 0};
+        if (T > 0) {
+          entry_read(e_kv, 0);
+          entry_read(e_iss, min(2 + kAhead, T - 1));
+        }
+        for (int ks = 2; ks <= T + 1; ++ks) {
+          step_begin(ks);
+          const bool do_issue = ks + kAhead < T;
+          const TileInfo tiss = entry_take(e_iss);
+          entry_read(e_iss, min(ks + 1 + kAhead, T - 1));
+          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, a.kv_scale, 0};
+          const TileInfo ti = entry_take(e_kv);
+          entry_read(e_kv, min(ks - 1, T - 1));
+          const int kv = ks - 2;
+          // LDS reads of this step, oldest first: the rescale votes of tile kv,
+          // its P^T fragments, then its transposed tile fragments; the votes
+          // are inspected once they arrive, while the rest is in flight.
+          int fl;
+          lds_b32<0>(fl, flags_addr + (kv & 1) * 4);
+          i32x4 pb[4];
+          const uint32_t pbase = aux_addr + P::kPOff + (kv & 1) * P::kPBufB + lane * 16;
+          static_for<0, 4>([&](auto nc) {
+            constexpr int nt = decltype(nc)::value;
+            lds_b128<nt * 1024>(pb[nt], pbase);
+          });
+          const uint32_t tile = ring_addr + (kv % kStages) * P::kStageB;
+          uint32_t tb[kTOff];
+#pragma unroll
+          for (int j = 0; j < kTOff; ++j) tb[j] = tile + t_off[j];
+          i32x2 rv[P::kMT];
+          static_for<0, P::kMT>([&](auto mc) {
+            constexpr int mt = decltype(mc)::value;
+            lds_tr8<64 * (mt >> 2)>(rv[mt], tb[mt & 3]);
+          });
+          wait_lgkm<4 + P::kMT>(fl);
+          const int fb = wave_uniform(fl);
+          if (fb != 0) {
+            // Rescale factors of heads whose reference max rose in tile kv.
+            i32x4 al;
+            lds_b128<0>(al, aux_addr + P::kAlphaOff + ((kv & 1) * 16 + l16) * 16);
+            wait_lgkm<0>(al);
+            const f32x4 alv = __builtin_bit_cast(f32x4, al);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+              if ((fb >> (8 * nt)) & 0xff)
+#pragma unroll
+                for (int mt = 0; mt < P::kMT; ++mt) st[4 * mt + nt] *= alv[nt];
+          }
+          static_for<0, P::kMT>([&](auto mc) {
+            constexpr int mt = decltype(mc)::value;
+            wait_lgkm<P::kMT - 1 - mt>(rv[mt]);
+            const i32x4 av = f8x8_to_f16x8(rv[mt][0], rv[mt][1]);
+            static_for<0, 4>([&](auto nc) {
+              constexpr int nt = decltype(nc)::value;
+              st[4 * mt + nt] = E::mfma(av, __builtin_bit_cast(typename E::vec, pb[nt]), st[4 * mt + nt]);
+            });
+            constexpr int n0 = mt * P::kPerWave / P::kVSpread;
+            constexpr int n1 = (mt + 1) * P::kPerWave / P::kVSpread;
+            static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
+          });
+          if (ti.last()) {
+            // Segment done: normalise by the score waves' head sums and store
+            // (O, slot s + g); the accumulators restart at zero.
+            const size_t slot = static_cast<size_t>(piece_b(ti.piece())) + g;
+            // fin[16nt + l16] for nt = 0..3
+            const uint32_t fa = aux_addr + P::kFinOff + ((nfin & 1) * 64 + l16) * 4;
+            int l0, l1, l2, l3;
+            lds_b32<0>(l0, fa);
+            lds_b32<64>(l1, fa);
+            lds_b32<128>(l2, fa);
+            lds_b32<192>(l3, fa);
+            wait_lgkm<0>(l0, l1);
+            wait_lgkm<0>(l2, l3);
+            const float lt[4] = {__int_as_float(l0), __int_as_float(l1), __int_as_float(l2),
+                                 __int_as_float(l3)};
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+              const float inv = lt[nt] > 0.f ? 1.f / lt[nt] : 0.f;
+              float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
+#pragma unroll
+              for (int mt = 0; mt < P::kMT; ++mt) {
+                *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
+                st[4 * mt + nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+              }
+            }
+            ++nfin;
+          }
+        }
+       }
+      } else if constexpr (kScorer) {
         i32x2 e_cur = {0, 0}, e_iss = {0, 0};
         if (T > 0) {
           entry_read(e_cur, 0);
@@ -1297,7 +1560,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             const float l_o = FP8 ? l_h : sum_xor32(sum_xor16(l_rnd));
             if (q4 == 0) {
               lds_store_b32(aux_addr + P::kFinOff + ((nfin & 1) * 64 + 16 * grp + l16) * 4, l_o);
-              const size_t slot = static_cast<size_t>(piece_s(ti.piece())) + g;
+              const size_t slot = static_cast<size_t>(piece_b(ti.piece())) + g;
               a.ws_lse[slot * a.Hq + head0 + 16 * grp + l16] =
                   l_h > 0.f ? (m_ref + fast_log2(l_h)) * kLn2 : -INFINITY;
             }
@@ -1392,7 +1655,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           if (ti.last()) {
             // Segment done: normalise by the score waves' head sums and store
             // (O, slot s + g); the accumulators restart at zero.
-            const size_t slot = static_cast<size_t>(piece_s(ti.piece())) + g;
+            const size_t slot = static_cast<size_t>(piece_b(ti.piece())) + g;
             // fin[16nt + l16] for nt = 0..3
             const uint32_t fa = aux_addr + P::kFinOff + ((nfin & 1) * 64 + l16) * 4;
             int l0, l1, l2, l3;
@@ -1439,6 +1702,18 @@ bool mla_supported(const dcp_attn_desc_t* d) {
          d->num_q_heads <= 256;
 }
 
+// The producer/consumer kernel: groups of 64 heads, blocks of a multiple of 32
+// tokens (a tile then lies inside one block, and per-lane copy offsets,
+// row * token stride, fit in 32 bits).
+static bool use_pp(const dcp_attn_desc_t* d) {
+  const long long elt = d->kv_dtype == DCP_BF16 ? 2 : 1;
+  return d->num_q_heads >= 64 && d->block_size % kT == 0 && d->kv_token_stride * elt * kT < (1ll << 30);
+}
+
+bool mla_sequence_pieces(const dcp_attn_desc_t* d) {
+  return d->kv_kind == DCP_KV_LATENT && use_pp(d);
+}
+
 template <int HG, bool FP8>
 static void launch_mla_hg(const MlaArgs& a, bool bs32, dim3 grid, hipStream_t stream) {
   if (bs32)
@@ -1473,7 +1748,7 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   const bool bs32 = d->block_size % kT == 0 && a.token_stride_b * kT < (1ll << 30);
   const int heads = d->num_q_heads < 64 ? d->num_q_heads : 64;
   const dim3 grid(kGroups, d->num_q_heads / heads);
-  if (bs32 && heads == 64) {
+  if (use_pp(d)) {
     if (fp8) hipLaunchKernelGGL(mla_pp_kernel<true>, grid, dim3(512), 0, stream, a);
     else hipLaunchKernelGGL(mla_pp_kernel<false>, grid, dim3(512), 0, stream, a);
     return hipGetLastError();

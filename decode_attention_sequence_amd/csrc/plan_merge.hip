@@ -56,17 +56,20 @@ WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim) 
 constexpr int kPlanLds = 6144;  // entries per mirrored array
 
 __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int seg_cost, int Hq,
-                                                    PlanHeader* hdr, int32_t* seg_off,
+                                                    int seq_pieces, PlanHeader* hdr, int32_t* seg_off,
                                                     int32_t* cost_off, int32_t* wg_start,
                                                     int32_t* seq_slots, float* lse) {
-  __shared__ int sums[1024];
-  __shared__ int costs[1024];
+  __shared__ int w_sum[16];
+  __shared__ int w_cost[16];
   __shared__ int l_seg[kPlanLds];
   __shared__ int l_cost[kPlanLds];
+  __shared__ int l_wg[kPlanLds];
   const bool mirror_s = S + 1 <= kPlanLds;
+  const bool mirror_g = G + 1 <= kPlanLds;
   const int t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
   const int per = (S + 1023) / 1024;
-  const int s0 = t * per;
+  const int s0 = min(S, t * per);
   const int s1 = min(S, s0 + per);
   int local = 0, local_c = 0;
   for (int s = s0; s < s1; ++s) {
@@ -74,18 +77,33 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
     local += nb;
     local_c += nb + (nb > 0 ? seg_cost : 0);
   }
-  sums[t] = local;
-  costs[t] = local_c;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = t >= off ? sums[t - off] : 0;
-    const int vc = t >= off ? costs[t - off] : 0;
-    __syncthreads();
-    sums[t] += v;
-    costs[t] += vc;
-    __syncthreads();
+  // Prefix sums over the threads' counts: an inclusive scan inside each wave
+  // (cross-lane moves, no barrier), then the sixteen wave totals.
+  int inc = local, inc_c = local_c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(inc, off), vc = __shfl_up(inc_c, off);
+    if (lane >= off) {
+      inc += v;
+      inc_c += vc;
+    }
   }
-  int run = sums[t] - local, run_c = costs[t] - local_c;
+  if (lane == 63) {
+    w_sum[wv] = inc;
+    w_cost[wv] = inc_c;
+  }
+  __syncthreads();
+  int run = inc - local, run_c = inc_c - local_c, total = 0, total_c = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int ws = w_sum[i], wc = w_cost[i];
+    if (i < wv) {
+      run += ws;
+      run_c += wc;
+    }
+    total += ws;
+    total_c += wc;
+  }
   for (int s = s0; s < s1; ++s) {
     const int nb = segment_blocks(m, s);
     run += nb;
@@ -104,13 +122,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
     l_cost[0] = 0;
   }
   if (t < 4) hdr->zero[t] = 0;
-  const int total = sums[1023];
-  const int total_c = costs[1023];
   if (t == 0) hdr->total = total;
   __syncthreads();  // seg_off and cost_off complete
   const int* so = mirror_s ? l_seg : seg_off;
   const int* co = mirror_s ? l_cost : cost_off;
-  const long long cc = max(1, (total_c + G - 1) / G);
+  // (Costs stay below 2^31: they count blocks of int32 table entries plus a
+  // few units per segment, so 32-bit arithmetic suffices.)
+  const unsigned cc = static_cast<unsigned>(max(1, (total_c + G - 1) / G));
   for (int g = t; g <= G; g += 1024) {
     const long long y = min(static_cast<long long>(g) * cc, static_cast<long long>(total_c));
     // last segment s < S with cost_off[s] <= y
@@ -125,21 +143,54 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
       x = so[lo] + static_cast<int>(max(0ll, o));
     }
     wg_start[g] = g == 0 ? 0 : x;
+    if (mirror_g) l_wg[g] = g == 0 ? 0 : x;
   }
-  // Slots of sequence b: segment s's pieces sit in slots s + g for the work
-  // groups g of its blocks, so b's pieces fill [lo, hi) except for gaps where
-  // a work-group boundary falls exactly on a segment boundary. Gap slots get
-  // LSE = -inf (an empty partial) so the merge can scan the whole range.
   // The work group of block i of segment s is floor(cost position / cc), the
   // cost position being cost_off[s] + seg_cost + i (the same split as above).
+  if (seq_pieces) {
+    // One partial per work group and sequence: sequence b's blocks (contiguous
+    // over its segments) lie in work groups g0..g1, whose partials sit in slots
+    // b + g0 .. b + g1. A work group in between without blocks leaves its slot
+    // unwritten: it gets LSE = -inf (an empty partial).
+    __syncthreads();  // wg_start complete
+    const int* wo = mirror_g ? l_wg : wg_start;
+    for (int b = t; b < m.batch; b += 1024) {
+      int s_first = -1, s_last = -1;
+      for (int s = b * m.D; s < (b + 1) * m.D; ++s)
+        if (so[s + 1] > so[s]) {
+          if (s_first < 0) s_first = s;
+          s_last = s;
+        }
+      int lo = 0, hi = 0;
+      if (s_first >= 0) {
+        const unsigned y0 = static_cast<unsigned>(co[s_first] + seg_cost);
+        const unsigned y1 = static_cast<unsigned>(co[s_last] + seg_cost + (so[s_last + 1] - so[s_last]) - 1);
+        const int g0 = min(G - 1, static_cast<int>(y0 / cc));
+        const int g1 = min(G - 1, static_cast<int>(y1 / cc));
+        lo = b + g0;
+        hi = b + g1 + 1;
+        for (int gg = g0 + 1; gg < g1; ++gg)
+          if (wo[gg] == wo[gg + 1])
+            for (int h = 0; h < Hq; ++h) lse[static_cast<size_t>(b + gg) * Hq + h] = -INFINITY;
+      }
+      seq_slots[2 * b] = lo;
+      seq_slots[2 * b + 1] = hi;
+    }
+    return;
+  }
+  // One partial per work group and segment: segment s's pieces sit in slots
+  // s + g for the work groups g of its blocks, so b's pieces fill [lo, hi)
+  // except for gaps where a work-group boundary falls exactly on a segment
+  // boundary. Gap slots get LSE = -inf (an empty partial) so the merge can
+  // scan the whole range.
   for (int b = t; b < m.batch; b += 1024) {
     int lo = 0, hi = 0;
     for (int s = b * m.D; s < (b + 1) * m.D; ++s) {
       const int nb = so[s + 1] - so[s];
       if (nb <= 0) continue;
-      const long long y0 = static_cast<long long>(co[s]) + seg_cost;
-      const int s_lo = s + static_cast<int>(min(static_cast<long long>(G - 1), y0 / cc));
-      const int s_hi = s + static_cast<int>(min(static_cast<long long>(G - 1), (y0 + nb - 1) / cc)) + 1;
+      const unsigned y0 = static_cast<unsigned>(co[s] + seg_cost);
+      const int s_lo = s + min(G - 1, static_cast<int>(y0 / cc));
+      const int s_hi = s + min(G - 1, static_cast<int>((y0 + nb - 1) / cc)) + 1;
       if (hi == 0) lo = s_lo;
       else
         for (int x = hi; x < s_lo; ++x)
@@ -151,9 +202,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
   }
 }
 
-hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, int Hq, WorkspaceView ws,
-                       hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, m, S, G, seg_cost, Hq, ws.header,
+hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, int Hq, bool seq_pieces,
+                       WorkspaceView ws, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, m, S, G, seg_cost, Hq,
+                     seq_pieces ? 1 : 0, ws.header,
                      ws.seg_off, ws.cost_off, ws.wg_start, ws.seq_slots, ws.lse);
   return hipGetLastError();
 }
@@ -175,119 +227,75 @@ struct PartialSource {
   __device__ __forceinline__ int slot(int b, int i, int) const { return i * B + b; }
 };
 
-// One work group per (sequence b, group of heads). kMergeSplits thread groups
-// each take every kMergeSplits-th partial; inside a group one thread owns 4
-// output values of one head. The LSEs of the group's heads are staged in LDS
-// once, every thread forms the weights exp(LSE_i - max) itself (the same max
-// in every group) and streams its 16 bytes of each partial row, kMergeRows
-// rows in flight; the groups' sums are added in LDS at the end. Rows are
-// loaded unconditionally (all lie inside the partial buffers) and the row of
-// an empty partial is dropped by a select, so garbage in it never reaches
-// the sum.
-constexpr int kMergeLse = 4096;   // LSE values staged in LDS per work group
-constexpr int kMergeRows = 4;     // partial rows loaded per round and thread
-constexpr int kMergeSplits = 4;   // thread groups splitting the partials
-constexpr int kMergeGroup = 256;  // most threads per group (heads x v_dim / 4)
+// One thread per 4 output values of one head of one sequence; a work group
+// holds kMergeThreads / (v_dim / 4) heads of one sequence, so for the usual
+// shapes the whole grid is resident at once. Each thread requests up to
+// kMergeRows partial rows (16 bytes of each) and their LSEs together, then
+// folds them into its sums with a running maximum (weights exp(LSE_i - max),
+// rescaled when the maximum rises): no LDS, no barriers, one memory round
+// trip for up to kMergeRows partials. Rows past the count are not loaded; the
+// row of an empty partial (LSE = -inf) is dropped by a select, so garbage in
+// it never reaches the sum.
+constexpr int kMergeRows = 16;      // partial rows in flight per thread
+constexpr int kMergeThreads = 256;  // threads per work group
 
-// Heads per merge work group for a value width: v_dim / 4 threads per head,
-// about 128 threads per group (one head when v_dim / 4 >= 128).
+// Heads per merge work group for a value width (v_dim / 4 threads per head).
 __host__ __device__ inline int merge_heads(int v_dim) {
   const int tph = v_dim / 4;
-  return tph >= 128 ? 1 : 128 / tph;
+  return tph >= kMergeThreads ? 1 : kMergeThreads / tph;
 }
 
 template <class Src>
-__global__ __launch_bounds__(kMergeSplits * kMergeGroup) void merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     Src src, const float* __restrict__ o_rows, const float* __restrict__ lse_rows, int H,
     int v_dim, void* out, int out_bf16, float* lse_out) {
-  __shared__ float s_lse[kMergeLse];
-  __shared__ f32x4 s_acc[kMergeSplits - 1][kMergeGroup];
-  __shared__ float s_w[kMergeSplits - 1][kMergeGroup];
   const int tph = v_dim >> 2;
   const int hpb = merge_heads(v_dim);
-  const int group = hpb * tph;
-  const int part = threadIdx.x / group;  // which thread group
-  const int tg = threadIdx.x % group;
+  const int hh = threadIdx.x / tph;
+  const int v4 = threadIdx.x % tph;
   // Heads vary fastest over the grid: consecutive work groups read rows of
-  // different heads (2 KB apart) rather than of one head (a slot apart).
+  // different heads rather than of one head (a slot apart).
   const int b = blockIdx.y;
-  const int h0 = blockIdx.x * hpb;
-  const int hh = tg / tph;
-  const int h = h0 + hh;
-  const int v4 = tg % tph;
+  const int h = blockIdx.x * hpb + hh;
+  if (hh >= hpb || h >= H) return;  // (no barriers below)
   const int n = src.count(b);
   const int f0 = src.first(b);
-  const int cap = kMergeLse / hpb;  // slots whose LSEs fit in LDS
-  const int ns = n < cap ? n : cap;
-  const bool live = h < H;
-  const int hc = live ? h : H - 1;  // (dead lanes read a valid row and store nothing)
-  const float* orow = o_rows + static_cast<size_t>(hc) * v_dim + 4 * v4;
-  auto row_of = [&](int k) -> const f32x4* {
-    return reinterpret_cast<const f32x4*>(orow + static_cast<size_t>(src.slot(b, k, f0)) * H * v_dim);
-  };
-  // The first LSE per thread and the first round of rows are requested
-  // together, before the LSEs are known (rows of empty partials are dropped
-  // by a select later), so the two round trips overlap.
-  auto stage_lse = [&](int i) -> float {
-    const int k = i / hpb, j = i - k * hpb;
-    return h0 + j < H ? lse_rows[static_cast<size_t>(src.slot(b, k, f0)) * H + h0 + j] : -INFINITY;
-  };
-  const int nl = ns * hpb;
-  const float l_first = static_cast<int>(threadIdx.x) < nl ? stage_lse(threadIdx.x) : -INFINITY;
-  f32x4 o[kMergeRows];
-  // Rows past n are not loaded (the branch is uniform over a thread group).
-  auto load_round = [&](int k0) {
+  const float* orow = o_rows + static_cast<size_t>(h) * v_dim + 4 * v4;
+  float m = -INFINITY;  // largest LSE so far
+  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < n; k0 += kMergeRows) {
+    f32x4 o[kMergeRows];
+    float l[kMergeRows];
 #pragma unroll
     for (int u = 0; u < kMergeRows; ++u) {
-      const int k = k0 + kMergeSplits * u;
+      l[u] = -INFINITY;
       o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (k < n) o[u] = *row_of(k);
-    }
-  };
-  load_round(part);
-  if (static_cast<int>(threadIdx.x) < nl) s_lse[threadIdx.x] = l_first;
-  for (int i = threadIdx.x + blockDim.x; i < nl; i += blockDim.x) s_lse[i] = stage_lse(i);
-  __syncthreads();
-  auto lse_of = [&](int k) -> float {
-    return k < ns ? s_lse[k * hpb + hh] : lse_rows[static_cast<size_t>(src.slot(b, k, f0)) * H + hc];
-  };
-  float top = -INFINITY;
-  for (int k = 0; k < n; ++k) top = fmaxf(top, lse_of(k));
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (top != -INFINITY) {
-    const float tl = top * kLog2e;
-    // Rows k0 + kMergeSplits * u of this thread group, already in o[].
-    auto add_round = [&](int k0) {
-#pragma unroll
-      for (int u = 0; u < kMergeRows; ++u) {
-        const int k = k0 + kMergeSplits * u;
-        const float l = k < n ? lse_of(k) : -INFINITY;
-        const bool on = l != -INFINITY;
-        const float w = on ? fast_exp2(l * kLog2e - tl) : 0.f;
-        wsum += w;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] += on ? w * o[u][c] : 0.f;
+      if (k0 + u < n) {
+        const size_t slot = static_cast<size_t>(src.slot(b, k0 + u, f0));
+        l[u] = lse_rows[slot * H + h];
+        o[u] = *reinterpret_cast<const f32x4*>(orow + slot * H * v_dim);
       }
-    };
-    add_round(part);
-    for (int k0 = part + kMergeSplits * kMergeRows; k0 < n; k0 += kMergeSplits * kMergeRows) {
-      load_round(k0);
-      add_round(k0);
+    }
+    float mr = m;
+#pragma unroll
+    for (int u = 0; u < kMergeRows; ++u) mr = fmaxf(mr, l[u]);
+    if (mr == -INFINITY) continue;  // only empty partials so far
+    const float ml = mr * kLog2e;
+    const float alpha = m == -INFINITY ? 0.f : fast_exp2(m * kLog2e - ml);
+    acc *= alpha;
+    wsum *= alpha;
+    m = mr;
+#pragma unroll
+    for (int u = 0; u < kMergeRows; ++u) {
+      const bool on = l[u] != -INFINITY;
+      const float w = on ? fast_exp2(l[u] * kLog2e - ml) : 0.f;
+      wsum += w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] += on ? w * o[u][c] : 0.f;
     }
   }
-  if (part > 0) {
-    s_acc[part - 1][tg] = acc;
-    s_w[part - 1][tg] = wsum;
-  }
-  __syncthreads();
-  if (part > 0 || !live) return;
-#pragma unroll
-  for (int p = 0; p < kMergeSplits - 1; ++p) {
-    acc += s_acc[p][tg];
-    wsum += s_w[p][tg];
-  }
-  if (top != -INFINITY) acc *= 1.0f / wsum;
+  if (m != -INFINITY) acc *= 1.0f / wsum;
   const size_t oidx = (static_cast<size_t>(b) * H + h) * v_dim + 4 * v4;
   if (out_bf16) {
     uint16_t* o16 = static_cast<uint16_t*>(out) + oidx;
@@ -297,10 +305,8 @@ __global__ __launch_bounds__(kMergeSplits * kMergeGroup) void merge_kernel(
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(out) + oidx) = acc;
   }
-  if (lse_out && v4 == 0) {
-    lse_out[static_cast<size_t>(b) * H + h] =
-        top == -INFINITY ? -INFINITY : top + fast_log2(wsum) * kLn2;
-  }
+  if (lse_out && v4 == 0)
+    lse_out[static_cast<size_t>(b) * H + h] = m == -INFINITY ? -INFINITY : m + fast_log2(wsum) * kLn2;
 }
 
 hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, int G, int Hq, int v_dim,
@@ -310,8 +316,7 @@ hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, int G, 
   PieceSource src{ws.seq_slots};
   const int hpb = merge_heads(v_dim);
   dim3 grid((Hq + hpb - 1) / hpb, m.batch);
-  hipLaunchKernelGGL(merge_kernel<PieceSource>, grid, dim3(kMergeSplits * hpb * (v_dim / 4)), 0,
-                     stream,
+  hipLaunchKernelGGL(merge_kernel<PieceSource>, grid, dim3(kMergeThreads), 0, stream,
                      src, ws.o, ws.lse, Hq,
                      v_dim, out, out_dtype == DCP_BF16 ? 1 : 0, lse_out);
   return hipGetLastError();
@@ -323,8 +328,7 @@ hipError_t launch_merge_partials(const float* o, const float* lse, int P, int B,
   PartialSource src{P, B};
   const int hpb = merge_heads(v_dim);
   dim3 grid((H + hpb - 1) / hpb, B);
-  hipLaunchKernelGGL(merge_kernel<PartialSource>, grid, dim3(kMergeSplits * hpb * (v_dim / 4)), 0,
-                     stream,
+  hipLaunchKernelGGL(merge_kernel<PartialSource>, grid, dim3(kMergeThreads), 0, stream,
                      src, o, lse, H, v_dim,
                      out, out_dtype == DCP_BF16 ? 1 : 0, lse_out);
   return hipGetLastError();

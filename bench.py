@@ -97,6 +97,60 @@ def cpu_baseline(w, o_gpu, lse_gpu, budget_s: float):
             "sample": sample}, parity
 
 
+def components(dcp, desc, dev, w, ws, iters: int = 20):
+    """The path's calls one by one, at the workload's real shapes: the
+    ownership remap, one shard's partial (the share one GPU of D would run;
+    shard 0, and the slowest shard), and the LSE merge of the D partials.
+    Wall time per call over `iters` back-to-back calls, bracketed by
+    synchronisation."""
+    import torch
+
+    spec = w.spec
+    D = spec.num_shards
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / iters
+
+    remap_ms = timed(lambda: dcp.block_remap(dev.block_table, dev.seq_lens, spec.block_size, D))
+    lt, ll = dcp.block_remap(dev.block_table, dev.seq_lens, spec.block_size, D)
+    o_parts = torch.empty((D, spec.batch, spec.num_q_heads, spec.v_dim), dtype=torch.float32,
+                          device="cuda")
+    lse_parts = torch.empty((D, spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
+    per_token = spec.kv_bytes_per_token()
+    shard_tokens = ll.sum(dim=1).cpu().numpy().astype(np.int64)
+    shard_ms = []
+    for r in range(D):
+        ltr, llr = lt[r].contiguous(), ll[r].contiguous()
+        shard_ms.append(timed(lambda: dcp.decode_partial(
+            desc, dev.q, dev.k_cache, dev.v_cache, dev.kv_scale, ltr, llr, workspace=ws,
+            o_partial=o_parts[r], lse_partial=lse_parts[r])))
+    out = torch.empty((spec.batch, spec.num_q_heads, spec.v_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
+    merge_ms = timed(lambda: dcp.lse_merge(o_parts, lse_parts, out=out, lse_out=lse))
+    merge_bytes = (o_parts.numel() + lse_parts.numel() + out.numel() + lse.numel()) * 4
+    slow = int(np.argmax(shard_ms))
+
+    def shard(r):
+        b = int(shard_tokens[r]) * per_token
+        return {"shard": r, "ms": round(shard_ms[r], 4), "kv_bytes": b,
+                "GBps": round(b / (shard_ms[r] * 1e-3) / 1e9, 1)}
+
+    return {
+        "note": "per call, wall time of back-to-back calls; each dcp_decode_partial includes its own plan and piece merge",
+        "block_remap_ms": round(remap_ms, 4),
+        "decode_partial_shard0": shard(0),
+        "decode_partial_slowest": shard(slow),
+        "lse_merge": {"partials": D, "ms": round(merge_ms, 4), "bytes": merge_bytes,
+                      "GBps": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1)},
+    }
+
+
 def copy_probe(mib: int):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -122,6 +176,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true",
+                    help="skip the per-call timings of remap, one shard's partial and the merge")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (counter scaling)")
     args = ap.parse_args()
@@ -219,6 +275,9 @@ def main():
             "kernel_ms": round(attn_ms, 4),
         },
     }
+    if not args.no_components:
+        log("timing the path's calls one by one")
+        result["components"] = components(dcp, desc, dev, w, ws)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         base, parity = cpu_baseline(w, out.cpu().numpy(), lse.cpu().numpy(), args.cpu_seconds)

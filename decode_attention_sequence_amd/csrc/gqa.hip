@@ -45,7 +45,12 @@ struct GqaArgs {
   float scale_log2;
 };
 
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// (Through the builtin, so the compiler's own wait insertion sees it; the empty
+// asm keeps memory accesses from moving across it.)
+__device__ __forceinline__ void wait_vm_all() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+  asm volatile("" ::: "memory");
+}
 
 // Row swizzle for rows of R chunks (R = 8 or 16).
 template <int R>

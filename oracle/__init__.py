@@ -8,7 +8,9 @@ It computes, in float64 with NumPy, exactly what the pages define:
 
 * interleaved block ownership (block j belongs to shard j mod D) and the
   global-to-local block-table remap -- "vLLM长序列推理优化：DCP切分KV Cache原理与实战",
-  sections 2.2 and 3.2;
+  sections 2.2 and 3.2; contiguous ownership (each shard one consecutive
+  chunk of a sequence) -- "Efficient Decode Context Parallelism with vLLM for
+  Long Context Workloads", section A2;
 * single-token softmax attention over a paged cache, unsharded, with GQA
   head sharing and absorbed-MLA latent rows -- "Efficient Decode Context
   Parallelism with vLLM for Long Context Workloads", section A2 (Compute step);
@@ -23,7 +25,9 @@ routines or the pages' worked examples; none is marked "parity unpinned".
 """
 from .codecs import bf16_to_f64, e4m3_to_f64
 from .paged import (
+    OWNERSHIPS,
     blocks_of,
+    chunk_of,
     gather_rows,
     local_lengths,
     owner_of_block,
@@ -45,6 +49,8 @@ from .attention import (
 )
 
 __all__ = [
+    "OWNERSHIPS",
+    "chunk_of",
     "bf16_to_f64",
     "e4m3_to_f64",
     "blocks_of",

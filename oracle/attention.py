@@ -117,17 +117,18 @@ def decode_reference(w, batch_indices=None):
     return out, lse
 
 
-def shard_positions(seq_len, block_size, num_shards, shard):
+def shard_positions(seq_len, block_size, num_shards, shard, ownership="interleaved"):
     """Token positions held by ``shard``: the tokens of its owned blocks."""
     pos = []
-    for j in range(blocks_of(seq_len, block_size)):
-        if owner_of_block(j, num_shards) == shard:
+    nb = blocks_of(seq_len, block_size)
+    for j in range(nb):
+        if owner_of_block(j, num_shards, ownership, nb) == shard:
             start = j * block_size
             pos.extend(range(start, start + tokens_in_block(j, seq_len, block_size)))
     return np.asarray(pos, dtype=np.int64)
 
 
-def shard_partials(w, num_shards=None, batch_indices=None):
+def shard_partials(w, num_shards=None, batch_indices=None, ownership="interleaved"):
     """Per-shard partial (O_r, LSE_r): [D, B, Hq, v_dim] and [D, B, Hq]."""
     spec = w.spec
     d = spec.num_shards if num_shards is None else num_shards
@@ -137,7 +138,7 @@ def shard_partials(w, num_shards=None, batch_indices=None):
     for b in bsel:
         q = query(w, b)
         for r in range(d):
-            pos = shard_positions(int(w.seq_lens[b]), spec.block_size, d, r)
+            pos = shard_positions(int(w.seq_lens[b]), spec.block_size, d, r, ownership)
             k, v = sequence_kv(w, b, pos)
             out[r, b], lse[r, b] = attend(q, k, v, spec.softmax_scale)
     return out, lse

@@ -11,18 +11,19 @@ The block index that is interleaved is the *logical* index of a block within
 its sequence (position t lives in logical block t // block_size at slot
 t % block_size). The last block of a sequence may be partly filled; it
 belongs to the shard that owns its index like any other block.
+
+Contiguous ownership, the alternative the pages also describe ("Efficient
+Decode Context Parallelism with vLLM for Long Context Workloads", section A2,
+and the vLLM blog post it summarises: a 200K-token request over 4 GPUs, GPU 0
+holding tokens 0-50K, GPU 1 50K-100K, and so on). At block granularity this
+reads: the nb blocks of a sequence form D consecutive chunks of
+c = ceil(nb / D) blocks, shard r owning blocks [r c, (r + 1) c) (the last
+chunks may be short or empty), with local index j - r c.
 """
 import numpy as np
 
 
-def owner_of_block(j: int, num_shards: int) -> int:
-    """Shard owning logical block j (section 2.2: block_idx % D)."""
-    return j % num_shards
-
-
-def local_index_of_block(j: int, num_shards: int) -> int:
-    """Position of logical block j in its owner's local table (section 3.2)."""
-    return j // num_shards
+OWNERSHIPS = ("interleaved", "contiguous")
 
 
 def blocks_of(seq_len: int, block_size: int) -> int:
@@ -30,33 +31,61 @@ def blocks_of(seq_len: int, block_size: int) -> int:
     return -(-int(seq_len) // int(block_size))
 
 
+def chunk_of(nb: int, num_shards: int) -> int:
+    """Blocks per shard under contiguous ownership: ceil(nb / D)."""
+    return -(-int(nb) // int(num_shards))
+
+
+def owner_of_block(j: int, num_shards: int, ownership: str = "interleaved", nb: int = 0) -> int:
+    """Shard owning logical block j: j % D (section 2.2), or, contiguous,
+    j // ceil(nb / D) for a sequence of nb blocks."""
+    if ownership == "interleaved":
+        return j % num_shards
+    if ownership == "contiguous":
+        return j // chunk_of(nb, num_shards)
+    raise ValueError(ownership)
+
+
+def local_index_of_block(j: int, num_shards: int, ownership: str = "interleaved", nb: int = 0) -> int:
+    """Position of logical block j in its owner's local table (section 3.2)."""
+    if ownership == "interleaved":
+        return j // num_shards
+    if ownership == "contiguous":
+        return j - owner_of_block(j, num_shards, ownership, nb) * chunk_of(nb, num_shards)
+    raise ValueError(ownership)
+
+
 def tokens_in_block(j: int, seq_len: int, block_size: int) -> int:
     """Valid tokens in logical block j of a sequence of seq_len tokens."""
     return max(0, min(block_size, seq_len - j * block_size))
 
 
-def shard_blocks(seq_len: int, block_size: int, num_shards: int, shard: int) -> list:
+def shard_blocks(seq_len: int, block_size: int, num_shards: int, shard: int,
+                 ownership: str = "interleaved") -> list:
     """Logical blocks of one sequence that ``shard`` owns, in local order."""
-    return [j for j in range(blocks_of(seq_len, block_size))
-            if owner_of_block(j, num_shards) == shard]
+    nb = blocks_of(seq_len, block_size)
+    return [j for j in range(nb) if owner_of_block(j, num_shards, ownership, nb) == shard]
 
 
-def local_lengths(seq_len: int, block_size: int, num_shards: int) -> list:
+def local_lengths(seq_len: int, block_size: int, num_shards: int,
+                  ownership: str = "interleaved") -> list:
     """Tokens each shard holds for one sequence, by counting its blocks."""
     out = [0] * num_shards
-    for j in range(blocks_of(seq_len, block_size)):
-        out[owner_of_block(j, num_shards)] += tokens_in_block(j, seq_len, block_size)
+    nb = blocks_of(seq_len, block_size)
+    for j in range(nb):
+        out[owner_of_block(j, num_shards, ownership, nb)] += tokens_in_block(j, seq_len, block_size)
     return out
 
 
-def remap_block_table(block_table, seq_lens, block_size: int, num_shards: int):
+def remap_block_table(block_table, seq_lens, block_size: int, num_shards: int,
+                      ownership: str = "interleaved"):
     """Global block table -> per-shard local tables (section 3.2).
 
     block_table: int32 [B, max_blocks] of physical block ids (logical j -> id).
     Returns (local_table int32 [D, B, ceil(max_blocks / D)] padded with -1,
              local_lens  int32 [D, B]).
-    Entry [r, b, i] is the physical id of the logical block j with
-    j % D == r and j // D == i.
+    Entry [r, b, i] is the physical id of the logical block j that shard r
+    owns at local index i (interleaved: j % D == r and j // D == i).
     """
     table = np.asarray(block_table)
     lens = np.asarray(seq_lens)
@@ -67,8 +96,8 @@ def remap_block_table(block_table, seq_lens, block_size: int, num_shards: int):
     for b in range(batch):
         n = min(blocks_of(lens[b], block_size), max_blocks)
         for j in range(n):
-            r = owner_of_block(j, num_shards)
-            i = local_index_of_block(j, num_shards)
+            r = owner_of_block(j, num_shards, ownership, n)
+            i = local_index_of_block(j, num_shards, ownership, n)
             local[r, b, i] = table[b, j]
             local_len[r, b] += tokens_in_block(j, int(lens[b]), block_size)
     return local, local_len

@@ -231,6 +231,59 @@ def check_ownership_bruteforce(O):
                 assert llen[r, b] == _local_len_closed_form(int(lens[b]), bs, d, r)
 
 
+def check_contiguous_worked_example(O):
+    g = _golden("contiguous_split.json")
+    L, bs, d = g["seq_len"], g["block_size"], g["num_shards"]
+    for r, (lo, hi) in enumerate(g["token_ranges"]):
+        pos = O.shard_positions(L, bs, d, r, ownership="contiguous")
+        assert len(pos) == hi - lo and int(pos[0]) == lo and int(pos[-1]) == hi - 1, r
+        assert bool(np.all(np.diff(pos) == 1)), r
+    assert O.local_lengths(L, bs, d, ownership="contiguous") == [hi - lo for lo, hi in
+                                                                  g["token_ranges"]]
+
+
+def check_contiguous_bruteforce(O):
+    """Contiguous ownership: shard r owns the r-th run of ceil(nb / D) blocks."""
+    for bs in (1, 3, 16):
+        for d in range(1, 10):
+            for L in list(range(0, 70)) + [97, 255, 299]:
+                nb = -(-L // bs)
+                c = -(-nb // d) if nb else 0
+                owners = []
+                for r in range(d):
+                    blocks = O.shard_blocks(L, bs, d, r, ownership="contiguous")
+                    # The first c blocks go to shard 0, the next c to shard 1, ...
+                    want = list(range(min(nb, r * c), min(nb, (r + 1) * c)))
+                    assert blocks == want, (L, bs, d, r, blocks)
+                    owners.extend([r] * len(blocks))
+                    for i, j in enumerate(blocks):
+                        assert O.local_index_of_block(j, d, "contiguous", nb) == i
+                assert len(owners) == nb
+                lens = O.local_lengths(L, bs, d, ownership="contiguous")
+                assert sum(lens) == L
+                for r in range(d):
+                    pos = O.shard_positions(L, bs, d, r, ownership="contiguous")
+                    assert len(pos) == lens[r]
+                    if len(pos):
+                        assert int(pos[0]) == r * c * bs and bool(np.all(np.diff(pos) == 1))
+    rng = np.random.default_rng(11)
+    for d in (1, 2, 3, 4, 8):
+        lens = rng.integers(0, 300, size=4)
+        bs = 16
+        mb = max(1, -(-int(lens.max()) // bs)) + 1
+        table = rng.permutation(10000)[: 4 * mb].reshape(4, mb).astype(np.int32)
+        local, llen = O.remap_block_table(table, lens, bs, d, ownership="contiguous")
+        for b in range(4):
+            nb = -(-int(lens[b]) // bs)
+            c = -(-nb // d) if nb else 0
+            for r in range(d):
+                row = [int(x) for x in local[r, b] if x >= 0]
+                assert row == [int(x) for x in table[b, min(nb, r * c):min(nb, (r + 1) * c)]]
+                assert all(int(x) == -1 for x in local[r, b, len(row):])
+                tok = max(0, min(int(lens[b]), (r + 1) * c * bs) - r * c * bs)
+                assert llen[r, b] == tok, (d, b, r)
+
+
 # ----------------------------------------------------------------- attention
 def _brute(q, k, v, scale):
     """Pure-Python loops, math.exp/math.log only."""
@@ -412,6 +465,8 @@ ALL_CHECKS = [
     check_even_split,
     check_remap_ragged,
     check_ownership_bruteforce,
+    check_contiguous_worked_example,
+    check_contiguous_bruteforce,
     check_attend_bruteforce,
     check_attend_sdpa,
     check_closed_forms,

@@ -42,8 +42,11 @@ MUTANTS = [
      "merged = o.sum(axis=0) / safe[..., None]", "(m, l) merge drops the rescale"),
     ("attention.py", "total = (l * factor).sum(axis=0)", "total = l.sum(axis=0)",
      "(m, l) merge sums l without rescale"),
-    ("attention.py", "if owner_of_block(j, num_shards) == shard:",
-     "if owner_of_block(j, num_shards) == (shard + 1) % num_shards:", "shard tokens shifted"),
+    ("attention.py", "if owner_of_block(j, num_shards, ownership, nb) == shard:",
+     "if owner_of_block(j, num_shards, ownership, nb) == (shard + 1) % num_shards:",
+     "shard tokens shifted"),
+    ("paged.py", "return j // chunk_of(nb, num_shards)",
+     "return min(num_shards - 1, j * num_shards // max(nb, 1))", "contiguous chunks balanced differently"),
     ("paged.py", "return j % num_shards", "return (j + 1) % num_shards", "owner off by one"),
     ("paged.py", "return j // num_shards", "return (j + 1) // num_shards", "local index off by one"),
     ("paged.py", "return cache[phys, pos % block_size]",

@@ -17,13 +17,17 @@ It computes, in float64 with NumPy, exactly what the pages define:
 * per-shard partial outputs with their log-sum-exp and the LSE merge
   O = sum_i exp(LSE_i) / sum_j exp(LSE_j) * O_i -- same page, summary
   section (merge equation) and A2 (AllGather + ReduceScatter step);
-* the equivalent (m, l) max/sum rescale merge -- "vLLM长序列推理优化", section 2.3.
+* the equivalent (m, l) max/sum rescale merge -- "vLLM长序列推理优化", section 2.3;
+* the KV append of a decode step into the block (and shard) owning the new
+  position, with E4M3 quantisation on write for fp8 caches -- "vLLM长序列推理优化",
+  sections 2.2, 3.2, 3.4 and 7 (the quantisation rule is a reading).
 
 No blocking, fusion or reordering is added beyond those definitions. Every
 function is pinned by the CPU tests to closed forms, brute force, library
 routines or the pages' worked examples; none is marked "parity unpinned".
 """
-from .codecs import bf16_to_f64, e4m3_to_f64
+from .codecs import E4M3_MAX, bf16_to_f64, e4m3_to_f64, f64_to_e4m3
+from .append import append_slot, kv_append, quantize_token_e4m3
 from .paged import (
     OWNERSHIPS,
     blocks_of,
@@ -49,6 +53,11 @@ from .attention import (
 )
 
 __all__ = [
+    "E4M3_MAX",
+    "f64_to_e4m3",
+    "append_slot",
+    "kv_append",
+    "quantize_token_e4m3",
     "OWNERSHIPS",
     "chunk_of",
     "bf16_to_f64",

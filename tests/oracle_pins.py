@@ -458,6 +458,108 @@ def check_merge_invariants(O):
     assert np.all(zo == 0) and np.all(zl == -np.inf)
 
 
+# ----------------------------------------------------------------- fp8 encode and KV append
+def _nearest_code_bruteforce(y, codes, vals):
+    """Nearest finite code to y by search; ties to the even code (mantissa bit 0)."""
+    a = min(abs(y), 448.0)
+    best = None
+    for c, v in zip(codes, vals):
+        if (c >> 7) or v < 0:
+            continue
+        dist = abs(v - a)
+        if best is None or dist < best[0] or (dist == best[0] and c % 2 == 0):
+            best = (dist, c)
+    return best[1] | (0x80 if math.copysign(1.0, y) < 0 else 0)
+
+
+def check_e4m3_encoder(O):
+    codes = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    vals = [float(x) for x in O.e4m3_to_f64(np.array(codes, dtype=np.uint8))]
+    # Every finite code is reproduced from its own value (including -0 -> 0x80).
+    got = O.f64_to_e4m3(np.array(vals))
+    assert got.tolist() == codes
+    # Midpoints between neighbours, values just off them, out-of-range values.
+    pos = sorted(set(v for v in vals if v >= 0))
+    probes = [0.0, -0.0, 1e-30, -1e-30, 449.0, 463.9, 464.0, 1e6, -1e6, 2.0 ** -10, 2.0 ** -11]
+    for lo, hi in zip(pos, pos[1:]):
+        mid = 0.5 * (lo + hi)
+        probes += [mid, -mid, mid * (1 + 2 ** -30), mid * (1 - 2 ** -30), lo + 0.3 * (hi - lo)]
+    rng = np.random.default_rng(3)
+    probes += list(rng.standard_normal(300) * np.exp2(rng.integers(-12, 9, 300)))
+    got = O.f64_to_e4m3(np.array(probes))
+    for y, c in zip(probes, got.tolist()):
+        assert c == _nearest_code_bruteforce(y, codes, vals), (y, c)
+    # torch's float8_e4m3fn cast (round to nearest even) on clipped random values.
+    x = np.clip(rng.standard_normal(20000).astype(np.float32) * 60, -448, 448)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.f64_to_e4m3(x.astype(np.float64)), ref)
+
+
+def check_quantize_token(O):
+    rng = np.random.default_rng(4)
+    for n in (1, 7, 64, 576):
+        for spread in (1e-3, 1.0, 300.0):
+            x = (rng.standard_normal(n) * spread).astype(np.float32)
+            codes, sigma = O.quantize_token_e4m3(x)
+            amax = float(np.max(np.abs(x)))
+            assert sigma.dtype == np.float32 and abs(float(sigma) * 448.0 - amax) <= amax * 2 ** -23
+            # The largest magnitude maps to the largest finite code.
+            k = int(np.argmax(np.abs(x)))
+            assert int(codes[k]) & 0x7F == 0x7E
+            # Dequantised values are within half a step of the E4M3 grid:
+            # relative 2^-4 for normal codes, absolute sigma * 2^-10 below 2^-6.
+            deq = O.e4m3_to_f64(codes) * float(sigma)
+            bound = np.maximum(np.abs(x) * 2.0 ** -4, float(sigma) * 2.0 ** -10) * (1 + 1e-6)
+            assert np.all(np.abs(deq - x) <= bound), (n, spread)
+            assert np.all(np.signbit(O.e4m3_to_f64(codes)) == np.signbit(x))
+    codes, sigma = O.quantize_token_e4m3(np.zeros(9, dtype=np.float32))
+    assert float(sigma) == 1.0 and not codes.any()
+    codes, sigma = O.quantize_token_e4m3(np.array([1e-38, -5e-39], dtype=np.float32))
+    assert float(sigma) == 1.0 and not codes.any()
+
+
+def check_kv_append_bruteforce(O):
+    rng = np.random.default_rng(6)
+    bs, pool, width = 4, 40, 6
+    for d in (1, 2, 3):
+        lens = [0, 5, 13, 23]
+        table = rng.permutation(pool)[: 4 * width].reshape(4, width).astype(np.int32)
+        local, _ = O.remap_block_table(table, np.array([p + 1 for p in lens]), bs, d)
+        k = rng.standard_normal((pool, bs, 2, 3)).astype(np.float32)
+        v = rng.standard_normal((pool, bs, 2, 5)).astype(np.float32)
+        kn = rng.standard_normal((4, 2, 3)).astype(np.float32)
+        vn = rng.standard_normal((4, 2, 5)).astype(np.float32)
+        for shard in [-1] + list(range(d)):
+            tab = table if shard < 0 else local[shard]
+            k2, v2, _ = O.kv_append(k, v, None, tab, lens, kn, vn, kv_dtype="f32", block_size=bs,
+                                    num_shards=d, shard=shard)
+            touched = np.zeros((pool, bs), dtype=bool)
+            for b, p in enumerate(lens):
+                j = p // bs
+                if shard >= 0 and j % d != shard:
+                    continue
+                phys = table[b, j]
+                assert np.array_equal(O.gather_rows(k2, table[b], [p], bs)[0], kn[b])
+                assert np.array_equal(O.gather_rows(v2, table[b], [p], bs)[0], vn[b])
+                touched[phys, p % bs] = True
+            assert np.array_equal(k2[~touched], k[~touched])
+            assert np.array_equal(v2[~touched], v[~touched])
+            want = sum(1 for p in lens if shard < 0 or (p // bs) % d == shard)
+            assert touched.sum() == want
+    # fp8 latent rows: codes and sigma land in the slot of each position.
+    lat = np.zeros((pool, bs, 8), dtype=np.uint8)
+    sc = np.full((pool, bs), -1.0, dtype=np.float32)
+    xn = rng.standard_normal((3, 8)).astype(np.float32)
+    table = rng.permutation(pool)[:15].reshape(3, 5).astype(np.int32)
+    pos = [3, 4, 17]
+    lat2, _, sc2 = O.kv_append(lat, None, sc, table, pos, xn, None, kv_dtype="fp8", block_size=bs)
+    for b, p in enumerate(pos):
+        phys, slot = table[b, p // bs], p % bs
+        deq = O.e4m3_to_f64(lat2[phys, slot]) * float(sc2[phys, slot])
+        assert np.all(np.abs(deq - xn[b]) <= np.abs(xn[b]) * 2.0 ** -4 + float(sc2[phys, slot]) * 2.0 ** -10)
+    assert int((sc2 != -1.0).sum()) == 3
+
+
 ALL_CHECKS = [
     check_codec_e4m3,
     check_codec_bf16,
@@ -475,4 +577,7 @@ ALL_CHECKS = [
     check_fp8_rows,
     check_shard_merge_equals_unsharded,
     check_merge_invariants,
+    check_e4m3_encoder,
+    check_quantize_token,
+    check_kv_append_bruteforce,
 ]

@@ -61,6 +61,19 @@ MUTANTS = [
     ("codecs.py", "(e - 7)", "(e - 8)", "e4m3 bias"),
     ("codecs.py", "np.ldexp(m / 8.0, -6)", "np.ldexp(m / 8.0, -7)", "e4m3 subnormal scale"),
     ("codecs.py", "(b << np.uint32(16))", "(b << np.uint32(15))", "bf16 shift"),
+    ("codecs.py", "n = np.rint(np.ldexp(a, -(e - 3)))", "n = np.floor(0.5 + np.ldexp(a, -(e - 3)))",
+     "e4m3 encode rounds ties away from even"),
+    ("codecs.py", "e = np.maximum(k.astype(np.int64) - 1, -6)", "e = np.maximum(k.astype(np.int64) - 1, -7)",
+     "e4m3 encode subnormal spacing"),
+    ("codecs.py", "a = np.minimum(np.abs(y), E4M3_MAX)", "a = np.abs(y)", "e4m3 encode not saturated"),
+    ("append.py", "sigma = amax / np.float32(E4M3_MAX)", "sigma = amax / np.float32(240.0)",
+     "fp8 scale for the wrong format maximum"),
+    ("append.py", "y = x32 * inv", "y = x32 * inv * np.float32(0.5)", "fp8 values not stretched to 448"),
+    ("append.py", "j = j // num_shards", "j = j % num_shards", "append local index"),
+    ("append.py", "return int(table_row[j]), position % block_size",
+     "return int(table_row[j]), (position + 1) % block_size", "append slot off by one"),
+    ("append.py", "if j % num_shards != shard:", "if j % num_shards == shard:",
+     "append writes the tokens of the other shards"),
 ]
 
 

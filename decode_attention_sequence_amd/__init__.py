@@ -6,7 +6,10 @@ the current HIP stream. If the library is not built, importing works but every
 call raises ``LibraryMissing`` -- there is no fallback implementation.
 
 Entry points (same names as the C ABI, without the ``dcp_`` prefix):
-  block_remap        global block table -> per-shard local tables (block j on shard j % D)
+  block_remap        global block table -> per-shard local tables (block j on shard j % D,
+                     or contiguous runs of ceil(nb / D) blocks with ownership="contiguous")
+  block_remap_update the same tables after sequences grew or shrank, remapping only changed blocks
+  kv_append          a decode step's KV write into the owning block (fp8: quantised on write)
   workspace_size     device workspace bytes for a descriptor
   decode_partial     one shard's partial output and log-sum-exp
   lse_merge          merge of D partials: O = sum_i exp(LSE_i) / sum_j exp(LSE_j) * O_i
@@ -23,7 +26,7 @@ import torch
 
 __all__ = [
     "AttnDesc", "DcpError", "LibraryMissing", "F32", "BF16", "FP8_E4M3", "KV_SEPARATE",
-    "KV_LATENT", "library_path", "lib", "make_desc", "block_remap", "workspace_size",
+    "KV_LATENT", "OWN_INTERLEAVED", "OWN_CONTIGUOUS", "library_path", "lib", "make_desc", "block_remap", "block_remap_update", "kv_append", "workspace_size",
     "decode_partial", "lse_merge", "decode_all_shards", "status_str", "version",
 ]
 
@@ -31,6 +34,8 @@ _LIB_PATH = Path(__file__).resolve().with_name("libdcp.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 KV_SEPARATE, KV_LATENT = 0, 1
+OWN_INTERLEAVED, OWN_CONTIGUOUS = 0, 1
+_OWNERSHIP = {"interleaved": OWN_INTERLEAVED, "contiguous": OWN_CONTIGUOUS}
 DCP_OK, DCP_ERR_INVALID_ARG, DCP_ERR_UNSUPPORTED, DCP_ERR_WORKSPACE, DCP_ERR_HIP = range(5)
 
 
@@ -91,6 +96,13 @@ def lib():
         L = ctypes.CDLL(str(_LIB_PATH))
         L.dcp_block_remap.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, _P]
         L.dcp_block_remap.restype = _I
+        L.dcp_block_remap_ex.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P]
+        L.dcp_block_remap_ex.restype = _I
+        L.dcp_block_remap_update.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]
+        L.dcp_block_remap_update.restype = _I
+        L.dcp_kv_append.argtypes = [ctypes.POINTER(AttnDesc), _I, _P, _P, _P, _P, _I, _I, _P,
+                                    _P, _P, _P, _P]
+        L.dcp_kv_append.restype = _I
         L.dcp_workspace_size.argtypes = [ctypes.POINTER(AttnDesc)]
         L.dcp_workspace_size.restype = ctypes.c_size_t
         L.dcp_decode_partial.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P,
@@ -131,6 +143,14 @@ def _check(status: int):
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: Optional[torch.Tensor], dtype, numel: int):
+    """Host-side size check of a buffer the library will index on the device."""
+    if t is None or not t.is_contiguous() or t.numel() != numel or (dtype and t.dtype != dtype):
+        got = None if t is None else (tuple(t.shape), t.dtype, t.is_contiguous())
+        raise DcpValueError(DCP_ERR_INVALID_ARG,
+                            f"expected a contiguous {dtype or ''} tensor of {numel} elements, got {got}")
 
 
 def _stream(device: torch.device):
@@ -208,8 +228,13 @@ def alloc_workspace(desc: AttnDesc, device) -> torch.Tensor:
 
 def block_remap(block_table: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
                 num_shards: int, local_table: Optional[torch.Tensor] = None,
-                local_lens: Optional[torch.Tensor] = None):
-    """-> (local_table int32 [D, B, ceil(max_blocks / D)], local_lens int32 [D, B])."""
+                local_lens: Optional[torch.Tensor] = None, ownership: str = "interleaved"):
+    """-> (local_table int32 [D, B, ceil(max_blocks / D)], local_lens int32 [D, B]).
+
+    ``ownership`` is "interleaved" (block j on shard j % D) or "contiguous"
+    (runs of ceil(nb / D) blocks per shard)."""
+    if ownership not in _OWNERSHIP:
+        raise DcpValueError(DCP_ERR_INVALID_ARG, f"unknown ownership {ownership!r}")
     B, mb = block_table.shape
     width = -(-mb // num_shards)
     dev = block_table.device
@@ -217,9 +242,57 @@ def block_remap(block_table: torch.Tensor, seq_lens: torch.Tensor, block_size: i
         local_table = torch.empty((num_shards, B, width), dtype=torch.int32, device=dev)
     if local_lens is None:
         local_lens = torch.empty((num_shards, B), dtype=torch.int32, device=dev)
-    _check(lib().dcp_block_remap(_ptr(block_table), _ptr(seq_lens), B, mb, block_size, num_shards,
-                                 _ptr(local_table), _ptr(local_lens), _stream(dev)))
+    _need(block_table, torch.int32, B * mb)
+    _need(seq_lens, torch.int32, B)
+    _need(local_table, torch.int32, num_shards * B * width)
+    _need(local_lens, torch.int32, num_shards * B)
+    _check(lib().dcp_block_remap_ex(_ptr(block_table), _ptr(seq_lens), B, mb, block_size,
+                                    num_shards, _OWNERSHIP[ownership], _ptr(local_table),
+                                    _ptr(local_lens), _stream(dev)))
     return local_table, local_lens
+
+
+def block_remap_update(block_table: torch.Tensor, old_seq_lens: torch.Tensor,
+                       seq_lens: torch.Tensor, block_size: int, num_shards: int,
+                       local_table: torch.Tensor, local_lens: torch.Tensor):
+    """Update (local_table, local_lens), the interleaved remap for ``old_seq_lens``, in place
+    to the remap for ``seq_lens``; only blocks that were added or dropped are touched."""
+    B, mb = block_table.shape
+    width = -(-mb // num_shards)
+    _need(block_table, torch.int32, B * mb)
+    _need(old_seq_lens, torch.int32, B)
+    _need(seq_lens, torch.int32, B)
+    _need(local_table, torch.int32, num_shards * B * width)
+    _need(local_lens, torch.int32, num_shards * B)
+    _check(lib().dcp_block_remap_update(_ptr(block_table), _ptr(old_seq_lens), _ptr(seq_lens), B,
+                                        mb, block_size, num_shards, _ptr(local_table),
+                                        _ptr(local_lens), _stream(block_table.device)))
+    return local_table, local_lens
+
+
+def kv_append(desc: AttnDesc, positions: torch.Tensor, k_new: torch.Tensor,
+              v_new: Optional[torch.Tensor], block_table: torch.Tensor, k_cache: torch.Tensor,
+              v_cache: Optional[torch.Tensor], kv_scale: Optional[torch.Tensor], shard: int = -1,
+              token_seq: Optional[torch.Tensor] = None):
+    """Write each new token's row(s) (k_new [T, Hkv, qk_dim] or latent [T, qk_dim]; v_new
+    [T, Hkv, v_dim]) into the cache slot of its position. shard=-1 takes the global block
+    table; shard=r takes shard r's local table and writes only the tokens r owns."""
+    n = int(positions.shape[0])
+    rows = desc.num_kv_heads if desc.kv_kind == KV_SEPARATE else 1
+    width = desc.max_blocks_per_seq if shard < 0 else -(-desc.max_blocks_per_seq // desc.num_shards)
+    _need(positions, torch.int32, n)
+    _need(k_new, None, n * rows * desc.qk_dim)
+    if desc.kv_kind == KV_SEPARATE:
+        _need(v_new, k_new.dtype, n * rows * desc.v_dim)
+    if token_seq is not None:
+        _need(token_seq, torch.int32, n)
+    _need(block_table, torch.int32, desc.batch * width)
+    if desc.kv_dtype == FP8_E4M3:
+        _need(kv_scale, torch.float32, desc.num_cache_blocks * desc.block_size)
+    _check(lib().dcp_kv_append(ctypes.byref(desc), n, _ptr(token_seq), _ptr(positions),
+                               _ptr(k_new), _ptr(v_new), _code(k_new), int(shard),
+                               _ptr(block_table), _ptr(k_cache), _ptr(v_cache), _ptr(kv_scale),
+                               _stream(k_cache.device)))
 
 
 def decode_partial(desc: AttnDesc, q, k_cache, v_cache, kv_scale, local_block_table,

@@ -19,7 +19,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 BUILD_DIR = ROOT / "_build"
 LIB = PKG / "libdcp.so"
-SOURCES = ["api.hip", "plan_merge.hip", "mla.hip", "gqa.hip"]
+SOURCES = ["api.hip", "plan_merge.hip", "mla.hip", "gqa.hip", "append.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU ops are switched off for all device code.

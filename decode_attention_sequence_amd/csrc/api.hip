@@ -118,19 +118,73 @@ size_t dcp_workspace_size(const dcp_attn_desc_t* d) {
   return a > b ? a : b;
 }
 
-dcp_status_t dcp_block_remap(const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
-                             int32_t max_blocks, int32_t block_size, int32_t num_shards,
-                             int32_t* local_block_table, int32_t* local_seq_lens,
-                             hipStream_t stream) {
+dcp_status_t dcp_block_remap_ex(const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                                int32_t max_blocks, int32_t block_size, int32_t num_shards,
+                                dcp_ownership_t ownership, int32_t* local_block_table,
+                                int32_t* local_seq_lens, hipStream_t stream) {
   if (!block_table || !seq_lens || !local_block_table || !local_seq_lens) return DCP_ERR_INVALID_ARG;
   if (batch < 1 || max_blocks < 1 || block_size < 1 || num_shards < 1) return DCP_ERR_INVALID_ARG;
+  if (ownership != DCP_OWN_INTERLEAVED && ownership != DCP_OWN_CONTIGUOUS) return DCP_ERR_INVALID_ARG;
   const long long width = (max_blocks + num_shards - 1) / num_shards;
   if (static_cast<long long>(batch) * max_blocks >= (1ll << 31) ||
       width * batch * num_shards >= (1ll << 31) ||
       static_cast<long long>(max_blocks) * block_size >= (1ll << 31))
     return DCP_ERR_INVALID_ARG;
   if (launch_remap(block_table, seq_lens, batch, max_blocks, block_size, num_shards,
-                   local_block_table, local_seq_lens, stream) != hipSuccess)
+                   ownership == DCP_OWN_CONTIGUOUS, local_block_table, local_seq_lens,
+                   stream) != hipSuccess)
+    return DCP_ERR_HIP;
+  return DCP_OK;
+}
+
+dcp_status_t dcp_block_remap(const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                             int32_t max_blocks, int32_t block_size, int32_t num_shards,
+                             int32_t* local_block_table, int32_t* local_seq_lens,
+                             hipStream_t stream) {
+  return dcp_block_remap_ex(block_table, seq_lens, batch, max_blocks, block_size, num_shards,
+                            DCP_OWN_INTERLEAVED, local_block_table, local_seq_lens, stream);
+}
+
+dcp_status_t dcp_block_remap_update(const int32_t* block_table, const int32_t* old_seq_lens,
+                                    const int32_t* seq_lens, int32_t batch, int32_t max_blocks,
+                                    int32_t block_size, int32_t num_shards,
+                                    int32_t* local_block_table, int32_t* local_seq_lens,
+                                    hipStream_t stream) {
+  if (!block_table || !old_seq_lens || !seq_lens || !local_block_table || !local_seq_lens)
+    return DCP_ERR_INVALID_ARG;
+  if (batch < 1 || max_blocks < 1 || block_size < 1 || num_shards < 1) return DCP_ERR_INVALID_ARG;
+  const long long width = (max_blocks + num_shards - 1) / num_shards;
+  if (static_cast<long long>(batch) * max_blocks >= (1ll << 31) ||
+      width * batch * num_shards >= (1ll << 31) ||
+      static_cast<long long>(max_blocks) * block_size >= (1ll << 31))
+    return DCP_ERR_INVALID_ARG;
+  if (launch_remap_update(block_table, old_seq_lens, seq_lens, batch, max_blocks, block_size,
+                          num_shards, local_block_table, local_seq_lens, stream) != hipSuccess)
+    return DCP_ERR_HIP;
+  return DCP_OK;
+}
+
+dcp_status_t dcp_kv_append(const dcp_attn_desc_t* d, int32_t num_tokens, const int32_t* token_seq,
+                           const int32_t* positions, const void* k_new, const void* v_new,
+                           dcp_dtype_t new_dtype, int32_t shard, const int32_t* block_table,
+                           void* k_cache, void* v_cache, float* kv_scale, hipStream_t stream) {
+  const dcp_status_t st = check_desc(d);
+  if (st != DCP_OK) return st;
+  if (num_tokens < 0 || shard < -1 || shard >= d->num_shards) return DCP_ERR_INVALID_ARG;
+  if (!valid_dtype(new_dtype)) return DCP_ERR_INVALID_ARG;
+  if (d->kv_dtype == DCP_FP8_E4M3 ? (new_dtype != DCP_BF16 && new_dtype != DCP_F32)
+                                  : new_dtype != d->kv_dtype)
+    return DCP_ERR_UNSUPPORTED;
+  if (num_tokens == 0 || d->batch == 0 || d->num_cache_blocks == 0) return DCP_OK;
+  if (!positions || !block_table || !k_new || !k_cache) return DCP_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(k_cache, 16)) return DCP_ERR_INVALID_ARG;
+  if (d->kv_kind == DCP_KV_SEPARATE &&
+      (!v_new || !v_cache || !aligned(v_new, 16) || !aligned(v_cache, 16)))
+    return DCP_ERR_INVALID_ARG;
+  if (d->kv_dtype == DCP_FP8_E4M3 && (!kv_scale || !aligned(kv_scale, 4)))
+    return DCP_ERR_INVALID_ARG;
+  if (launch_kv_append(d, num_tokens, token_seq, positions, k_new, v_new, new_dtype, shard,
+                       block_table, k_cache, v_cache, kv_scale, stream) != hipSuccess)
     return DCP_ERR_HIP;
   return DCP_OK;
 }

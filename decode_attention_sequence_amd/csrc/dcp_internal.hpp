@@ -197,7 +197,17 @@ hipError_t launch_merge_partials(const float* o, const float* lse, int P, int B,
                                  void* out, dcp_dtype_t out_dtype, float* lse_out,
                                  hipStream_t stream);
 hipError_t launch_remap(const int32_t* table, const int32_t* lens, int B, int max_blocks, int bs,
-                        int D, int32_t* local_table, int32_t* local_lens, hipStream_t stream);
+                        int D, bool contiguous, int32_t* local_table, int32_t* local_lens,
+                        hipStream_t stream);
+
+hipError_t launch_remap_update(const int32_t* table, const int32_t* old_lens, const int32_t* lens,
+                               int B, int max_blocks, int bs, int D, int32_t* local_table,
+                               int32_t* local_lens, hipStream_t stream);
+
+hipError_t launch_kv_append(const dcp_attn_desc_t* d, int n_tokens, const int32_t* token_seq,
+                            const int32_t* positions, const void* k_new, const void* v_new,
+                            dcp_dtype_t new_dtype, int shard, const int32_t* table, void* k_cache,
+                            void* v_cache, float* kv_scale, hipStream_t stream);
 
 struct AttnLaunch {
   const dcp_attn_desc_t* desc;

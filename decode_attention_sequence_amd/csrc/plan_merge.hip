@@ -336,10 +336,15 @@ hipError_t launch_merge_partials(const float* o, const float* lse, int P, int B,
 
 // ------------------------------------------------------------------ remap
 // One thread per local-table entry [r, b, i]; entries with i == 0 also write
-// the shard's token count for sequence b.
+// the shard's token count for sequence b. Interleaved ownership: entry i of
+// shard r is logical block r + D*i. Contiguous ownership (the 200K-token
+// four-way split of the DCP blog page, section A2): a sequence of nb blocks is
+// cut into runs of c = ceil(nb / D) blocks and entry i of shard r is logical
+// block r*c + i.
 __global__ __launch_bounds__(256) void remap_kernel(const int32_t* __restrict__ table,
                                                     const int32_t* __restrict__ lens, int B,
                                                     int max_blocks, int bs, int D, int width,
+                                                    int contiguous,
                                                     int32_t* __restrict__ local_table,
                                                     int32_t* __restrict__ local_lens) {
   const long long total = static_cast<long long>(D) * B * width;
@@ -352,6 +357,18 @@ __global__ __launch_bounds__(256) void remap_kernel(const int32_t* __restrict__ 
   const long long cap = static_cast<long long>(max_blocks) * bs;
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int nb = static_cast<int>((L + bs - 1) / bs);
+  if (contiguous) {
+    const int c = (nb + D - 1) / D;  // c <= width because nb <= max_blocks
+    const int j = r * c + i;
+    local_table[idx] = (i < c && j < nb) ? table[static_cast<size_t>(b) * max_blocks + j] : -1;
+    if (i == 0) {
+      const long long lo = static_cast<long long>(r) * c * bs;
+      const long long hi = lo + static_cast<long long>(c) * bs;
+      const long long n = (hi < L ? hi : L) - lo;
+      local_lens[static_cast<size_t>(r) * B + b] = static_cast<int32_t>(n > 0 ? n : 0);
+    }
+    return;
+  }
   const int j = r + D * i;
   local_table[idx] = j < nb ? table[static_cast<size_t>(b) * max_blocks + j] : -1;
   if (i == 0) {
@@ -362,13 +379,15 @@ __global__ __launch_bounds__(256) void remap_kernel(const int32_t* __restrict__ 
 }
 
 hipError_t launch_remap(const int32_t* table, const int32_t* lens, int B, int max_blocks, int bs,
-                        int D, int32_t* local_table, int32_t* local_lens, hipStream_t stream) {
+                        int D, bool contiguous, int32_t* local_table, int32_t* local_lens,
+                        hipStream_t stream) {
   const int width = (max_blocks + D - 1) / D;
   const long long total = static_cast<long long>(D) * B * width;
   const int threads = 256;
   const long long blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(remap_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream,
-                     table, lens, B, max_blocks, bs, D, width, local_table, local_lens);
+                     table, lens, B, max_blocks, bs, D, width, contiguous ? 1 : 0, local_table,
+                     local_lens);
   return hipGetLastError();
 }
 

@@ -118,6 +118,77 @@ dcp_status_t dcp_block_remap(const int32_t* block_table, const int32_t* seq_lens
                              int32_t* local_block_table, int32_t* local_seq_lens,
                              hipStream_t stream);
 
+/* Which shard owns which logical block of a sequence.
+ *   DCP_OWN_INTERLEAVED: block j on shard j % D at local index j / D
+ *     ("vLLM长序列推理优化", section 2.2); the layout every decode entry point
+ *     that takes a global table assumes.
+ *   DCP_OWN_CONTIGUOUS: a sequence of nb blocks is cut into D runs of
+ *     c = ceil(nb / D) blocks; block j on shard j / c at local index j % c
+ *     (the 200K-token split over four GPUs, 0-50K on the first, in section A2
+ *     of "Efficient Decode Context Parallelism with vLLM for Long Context
+ *     Workloads"). The runs depend on the sequence's current length. */
+typedef enum { DCP_OWN_INTERLEAVED = 0, DCP_OWN_CONTIGUOUS = 1 } dcp_ownership_t;
+
+/* dcp_block_remap under a chosen ownership. Same arguments and output layout;
+ * entry [r, b, i] is the physical id of the i-th block shard r owns of
+ * sequence b. Any other ownership value is DCP_ERR_INVALID_ARG.
+ * dcp_block_remap is this call with DCP_OWN_INTERLEAVED. */
+dcp_status_t dcp_block_remap_ex(const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                                int32_t max_blocks, int32_t block_size, int32_t num_shards,
+                                dcp_ownership_t ownership, int32_t* local_block_table,
+                                int32_t* local_seq_lens, hipStream_t stream);
+
+/* Incremental form of dcp_block_remap (interleaved ownership) for a decode
+ * step: only the blocks a sequence gained or lost are remapped, as in
+ * "vLLM长序列推理优化", section 6.2.
+ *   local_block_table, local_seq_lens hold dcp_block_remap's output for
+ *   old_seq_lens on entry and for seq_lens on return, provided block_table
+ *   entries below min(old, new) block counts did not change.
+ *   Entries of blocks [nb(old), nb(new)) are written from block_table; if
+ *   a sequence shrank, entries of blocks [nb(new), nb(old)) become -1. Every
+ *   local_seq_lens entry is recomputed. Other arguments as in dcp_block_remap.
+ * Cost O(batch * num_shards + changed blocks). Bit-exact integer work. */
+dcp_status_t dcp_block_remap_update(const int32_t* block_table, const int32_t* old_seq_lens,
+                                    const int32_t* seq_lens, int32_t batch, int32_t max_blocks,
+                                    int32_t block_size, int32_t num_shards,
+                                    int32_t* local_block_table, int32_t* local_seq_lens,
+                                    hipStream_t stream);
+
+/* KV write of a decode step: stores each new token's cached row(s) in the
+ * block that owns its position (sections 2.2, 3.2 and 3.4 of
+ * "vLLM长序列推理优化"; keys arrive after the rotary embedding and are
+ * stored as given).
+ *   num_tokens  tokens to write (0 is a no-op)
+ *   token_seq   [num_tokens] int32 sequence (block-table row) of each token,
+ *               or NULL for token i in sequence i
+ *   positions   [num_tokens] int32 position p of each token in its sequence;
+ *               it goes to logical block p / block_size, slot p % block_size
+ *   k_new       DCP_KV_SEPARATE: [num_tokens, num_kv_heads, qk_dim];
+ *               DCP_KV_LATENT: [num_tokens, qk_dim] (16-byte aligned)
+ *   v_new       [num_tokens, num_kv_heads, v_dim] for DCP_KV_SEPARATE, else ignored
+ *   new_dtype   element type of k_new / v_new: desc->kv_dtype for F32 and
+ *               BF16 caches (a copy); BF16 or F32 for an FP8_E4M3 cache
+ *   shard       -1: block_table is the global table [batch, max_blocks_per_seq];
+ *               r in [0, num_shards): block_table is shard r's local table
+ *               [batch, ceil(max_blocks_per_seq / num_shards)] and only tokens
+ *               whose block j satisfies j % num_shards == r are written (at
+ *               local index j / num_shards), the others are skipped
+ *   k_cache, v_cache, kv_scale  the cache as described by desc (written)
+ * FP8 caches: per token, sigma = amax / 448 with amax the row's largest
+ * magnitude, and each code is the nearest E4M3 value (ties to even) of
+ * x * (448 / amax), both quotients rounded once in fp32; a row with amax 0
+ * (or 448 / amax beyond fp32) is stored as zero codes with sigma = 1. Inputs
+ * must be finite. The pages name an FP8 KV cache (section 7) without a rule;
+ * this one is a reading.
+ * Tokens with a negative position, a sequence outside [0, batch), a block
+ * past the table width or a table entry outside [0, num_cache_blocks) are
+ * skipped. Two tokens for the same slot in one call race. */
+dcp_status_t dcp_kv_append(const dcp_attn_desc_t* desc, int32_t num_tokens,
+                           const int32_t* token_seq, const int32_t* positions, const void* k_new,
+                           const void* v_new, dcp_dtype_t new_dtype, int32_t shard,
+                           const int32_t* block_table, void* k_cache, void* v_cache,
+                           float* kv_scale, hipStream_t stream);
+
 /* Bytes of device workspace dcp_decode_partial and dcp_decode_all_shards need
  * for this descriptor (the larger of the two), or 0 if the descriptor is
  * invalid or unsupported. The workspace holds split partials and a small

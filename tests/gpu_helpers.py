@@ -84,12 +84,13 @@ def run_all_shards(w, out_dtype=dcp.F32, num_shards=None):
     return o, lse, dev, desc
 
 
-def run_per_shard(w, dev=None, num_shards=None):
+def run_per_shard(w, dev=None, num_shards=None, ownership="interleaved"):
     """remap -> decode_partial for every shard -> (O_r [D,B,H,Dv], LSE_r [D,B,H])."""
     dev = dev or W.to_torch(w)
     d = w.spec.num_shards if num_shards is None else num_shards
     desc = desc_for(w, dev, num_shards=d)
-    lt, ll = dcp.block_remap(dev.block_table, dev.seq_lens, w.spec.block_size, d)
+    lt, ll = dcp.block_remap(dev.block_table, dev.seq_lens, w.spec.block_size, d,
+                             ownership=ownership)
     ws = dcp.alloc_workspace(desc, dev.q.device)
     outs, lses = [], []
     for r in range(d):

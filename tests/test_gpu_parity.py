@@ -62,6 +62,19 @@ def test_any_shard_count_gives_unsharded_result(num_shards):
         compare(op[r], lp[r], opr[r], lpr[r], **TOL["bf16"], label=f"D={num_shards} r={r}")
 
 
+@pytest.mark.parametrize("spec", SMALL[1:4], ids=lambda s: s.name)
+def test_contiguous_ownership_partials_and_merge(spec):
+    """Contiguous runs of blocks per shard: other partials, the same merged result."""
+    w = W.make(spec)
+    op_ref, lp_ref = oracle.shard_partials(w, ownership="contiguous")
+    op, lp, _, _ = run_per_shard(w, ownership="contiguous")
+    for r in range(spec.num_shards):
+        compare(op[r], lp[r], op_ref[r], lp_ref[r], **TOL[spec.kv_dtype], label=f"shard {r}")
+    o, lse = dcp.lse_merge(op, lp)
+    o_ref, lse_ref = oracle.decode_reference(w)
+    compare(o, lse, o_ref, lse_ref, **TOL[spec.kv_dtype], label="merged contiguous shards")
+
+
 def test_bf16_output():
     spec = W.scaled(W.SPECS["mla_bf16_b64_bimodal"], 16, 64)
     w = W.make(spec)

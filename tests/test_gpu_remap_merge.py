@@ -20,10 +20,10 @@ def _gpu():
     need_gpu()
 
 
-def _remap_gpu(table, lens, bs, d):
+def _remap_gpu(table, lens, bs, d, ownership="interleaved"):
     t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).cuda()
     l = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda()
-    lt, ll = dcp.block_remap(t, l, bs, d)
+    lt, ll = dcp.block_remap(t, l, bs, d, ownership=ownership)
     torch.cuda.synchronize()
     return lt.cpu().numpy(), ll.cpu().numpy()
 
@@ -46,19 +46,52 @@ def test_remap_full_size_tables(name):
     assert np.array_equal(lt, rt) and np.array_equal(ll, rl)
 
 
-def test_remap_edges():
+@pytest.mark.parametrize("ownership", oracle.OWNERSHIPS)
+def test_remap_edges(ownership):
     rng = np.random.default_rng(5)
     for bs in (1, 3, 16, 64):
         for d in (1, 2, 3, 4, 7, 8, 9):
             lens = np.array([0, 1, bs - 1, bs, bs + 1, 2 * bs, d * bs - 1, d * bs, d * bs + 1,
-                             5 * d * bs + 3], dtype=np.int32)
+                             5 * d * bs + 3, (d - 1) * bs + 1], dtype=np.int32)
             lens = np.maximum(lens, 0)
             mb = int(-(-lens.max() // bs)) + 1
             table = rng.permutation(100000)[: len(lens) * mb].reshape(len(lens), mb).astype(np.int32)
-            lt, ll = _remap_gpu(table, lens, bs, d)
-            rt, rl = oracle.remap_block_table(table, lens, bs, d)
+            lt, ll = _remap_gpu(table, lens, bs, d, ownership)
+            rt, rl = oracle.remap_block_table(table, lens, bs, d, ownership)
             assert np.array_equal(lt, rt), (bs, d)
             assert np.array_equal(ll, rl), (bs, d)
+
+
+def test_remap_contiguous_page_example():
+    g = json.loads((GOLDEN / "contiguous_split.json").read_text())
+    bs, d, L = g["block_size"], g["num_shards"], g["seq_len"]
+    nb = L // bs
+    table = (7 + np.arange(nb, dtype=np.int32))[None, :]
+    lt, ll = _remap_gpu(table, np.array([L]), bs, d, "contiguous")
+    assert ll[:, 0].tolist() == [hi - lo for lo, hi in g["token_ranges"]]
+    for r, (lo, hi) in enumerate(g["token_ranges"]):
+        row = lt[r, 0]
+        assert row.tolist() == (7 + np.arange(lo // bs, hi // bs)).tolist()
+
+
+@pytest.mark.parametrize("name", ["mla_bf16_b64_bimodal", "mla_fp8_b128_bimodal"])
+def test_remap_contiguous_full_size_tables(name):
+    spec = W.SPECS[name]
+    lens = W.seq_lengths(spec)
+    table, _ = W.build_block_table(lens, spec.block_size, spec.seed)
+    lt, ll = _remap_gpu(table, lens, spec.block_size, spec.num_shards, "contiguous")
+    rt, rl = oracle.remap_block_table(table, lens, spec.block_size, spec.num_shards, "contiguous")
+    assert np.array_equal(lt, rt) and np.array_equal(ll, rl)
+
+
+def test_remap_rejects_unknown_ownership():
+    t = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    l = torch.ones(1, dtype=torch.int32, device="cuda")
+    out_t = torch.empty((2, 1, 2), dtype=torch.int32, device="cuda")
+    out_l = torch.empty((2, 1), dtype=torch.int32, device="cuda")
+    status = dcp.lib().dcp_block_remap_ex(t.data_ptr(), l.data_ptr(), 1, 4, 16, 2, 5,
+                                          out_t.data_ptr(), out_l.data_ptr(), None)
+    assert status == dcp.DCP_ERR_INVALID_ARG
 
 
 def _rand_partials(p, b, h, dv, seed):

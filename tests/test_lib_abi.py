@@ -28,7 +28,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = dcp.lib()
     names = declared_functions()
-    assert set(names) >= {"dcp_block_remap", "dcp_workspace_size", "dcp_decode_partial",
+    assert set(names) >= {"dcp_block_remap", "dcp_block_remap_ex", "dcp_workspace_size", "dcp_decode_partial",
                           "dcp_lse_merge", "dcp_decode_all_shards", "dcp_status_str",
                           "dcp_version"}
     for n in names:
@@ -153,6 +153,11 @@ def test_remap_and_merge_argument_errors():
     assert L.dcp_block_remap(None, FAKE, 1, 1, 1, 1, FAKE, FAKE, None) == dcp.DCP_ERR_INVALID_ARG
     assert L.dcp_block_remap(FAKE, FAKE, 1, 1, 1, 0, FAKE, FAKE, None) == dcp.DCP_ERR_INVALID_ARG
     assert L.dcp_block_remap(FAKE, FAKE, 0, 1, 1, 1, FAKE, FAKE, None) == dcp.DCP_ERR_INVALID_ARG
+    for own in (-1, 2, 99):
+        assert L.dcp_block_remap_ex(FAKE, FAKE, 1, 1, 1, 1, own, FAKE, FAKE, None) == \
+            dcp.DCP_ERR_INVALID_ARG
+    assert L.dcp_block_remap_ex(FAKE, FAKE, 1, 1, 1, 0, dcp.OWN_CONTIGUOUS, FAKE, FAKE, None) == \
+        dcp.DCP_ERR_INVALID_ARG
     assert L.dcp_lse_merge(FAKE, FAKE, 0, 1, 1, 4, FAKE, dcp.F32, None, None) == \
         dcp.DCP_ERR_INVALID_ARG
     assert L.dcp_lse_merge(FAKE, FAKE, 2, 1, 1, 6, FAKE, dcp.F32, None, None) == \

@@ -18,6 +18,9 @@ It computes, in float64 with NumPy, exactly what the pages define:
   O = sum_i exp(LSE_i) / sum_j exp(LSE_j) * O_i -- same page, summary
   section (merge equation) and A2 (AllGather + ReduceScatter step);
 * the equivalent (m, l) max/sum rescale merge -- "vLLM长序列推理优化", section 2.3;
+* multi-token (MTP / draft) decode: q_len query tokens per sequence at the
+  last q_len positions, each seeing the positions up to its own (a reading;
+  the DCP blog page lists MTP as future work in A5);
 * the KV append of a decode step into the block (and shard) owning the new
   position, with E4M3 quantisation on write for fp8 caches -- "vLLM长序列推理优化",
   sections 2.2, 3.2, 3.4 and 7 (the quantisation rule is a reading).
@@ -47,6 +50,7 @@ from .attention import (
     ml_merge,
     ml_partials,
     query,
+    query_positions,
     sequence_kv,
     shard_partials,
     shard_positions,
@@ -76,6 +80,7 @@ __all__ = [
     "ml_merge",
     "ml_partials",
     "query",
+    "query_positions",
     "sequence_kv",
     "shard_partials",
     "shard_positions",

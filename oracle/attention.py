@@ -16,8 +16,15 @@ Definitions followed (page titles, then the passage):
     m_i = max S_i, l_i = sum exp(S_i - m_i), O_i = exp(S_i - m_i) V_i; then
     m = max m_i, l = sum_i l_i exp(m_i - m), O = sum_i O_i exp(m_i - m) / l.
   * Same page, section 3.4: the cache holds keys after the rotary embedding
-    is applied, so decode attention needs no positions and no mask: all
+    is applied, so single-token decode needs no positions and no mask: all
     seq_len cached tokens are visible.
+  * Multi-token decode (MTP / speculative drafts; named as DCP future work on
+    the DCP blog page, A5, future work): a sequence carries q_len query tokens, the last
+    q_len cached positions L - q_len .. L - 1. The pages give no masking
+    rule; the reading used here is the usual causal one: query t (at position
+    L - q_len + t) sees the positions p <= L - q_len + t. Under DCP a shard
+    sees only its own blocks, so it needs the global position of each local
+    token (block j of the sequence holds positions j*bs .. j*bs + bs - 1).
 
 Readings where the pages are silent: scores are softmax_scale * q.k with the
 scale a runtime argument; LSE is the natural log over the scaled scores;
@@ -73,8 +80,14 @@ def _decode(values, dtype):
 
 
 def query(w, b):
-    """Query of sequence b as float64 [Hq, qk_dim]."""
+    """Queries of sequence b as float64 [q_len * Hq, qk_dim], token-major."""
     return _decode(w.q[b], w.spec.q_dtype)
+
+
+def query_positions(w, b):
+    """Positions of the q_len query tokens of sequence b: L - q_len + t."""
+    n = w.spec.q_len
+    return [int(w.seq_lens[b]) - n + t for t in range(n)]
 
 
 def sequence_kv(w, b, positions=None):
@@ -103,17 +116,23 @@ def sequence_kv(w, b, positions=None):
 
 
 def decode_reference(w, batch_indices=None):
-    """Unsharded attention for every (b, h): O [B, Hq, v_dim], LSE [B, Hq].
+    """Unsharded attention for every (b, t, h): O [B, q_len * Hq, v_dim],
+    LSE [B, q_len * Hq]; query t sees the positions up to its own.
 
     Rows of sequences not in ``batch_indices`` are left as NaN.
     """
     spec = w.spec
+    hq, n = spec.num_q_heads, spec.q_len
     bsel = range(spec.batch) if batch_indices is None else batch_indices
-    out = np.full((spec.batch, spec.num_q_heads, spec.v_dim), np.nan)
-    lse = np.full((spec.batch, spec.num_q_heads), np.nan)
+    out = np.full((spec.batch, n * hq, spec.v_dim), np.nan)
+    lse = np.full((spec.batch, n * hq), np.nan)
     for b in bsel:
-        k, v = sequence_kv(w, b)
-        out[b], lse[b] = attend(query(w, b), k, v, spec.softmax_scale)
+        k, v = sequence_kv(w, b)  # row i holds position i
+        q = query(w, b)
+        for t, p in enumerate(query_positions(w, b)):
+            rows = slice(t * hq, (t + 1) * hq)
+            seen = max(0, p + 1)
+            out[b, rows], lse[b, rows] = attend(q[rows], k[:seen], v[:seen], spec.softmax_scale)
     return out, lse
 
 
@@ -128,19 +147,30 @@ def shard_positions(seq_len, block_size, num_shards, shard, ownership="interleav
     return np.asarray(pos, dtype=np.int64)
 
 
-def shard_partials(w, num_shards=None, batch_indices=None, ownership="interleaved"):
-    """Per-shard partial (O_r, LSE_r): [D, B, Hq, v_dim] and [D, B, Hq]."""
+def shard_partials(w, num_shards=None, batch_indices=None, ownership="interleaved",
+                   q_pos=None):
+    """Per-shard partial (O_r, LSE_r): [D, B, q_len * Hq, v_dim] and [D, B, q_len * Hq].
+
+    Query t of sequence b sees the shard's positions p <= q_pos[b] + t
+    (default q_pos[b] = L_b - q_len, the last q_len cached positions).
+    """
     spec = w.spec
+    hq, n = spec.num_q_heads, spec.q_len
     d = spec.num_shards if num_shards is None else num_shards
     bsel = range(spec.batch) if batch_indices is None else batch_indices
-    out = np.full((d, spec.batch, spec.num_q_heads, spec.v_dim), np.nan)
-    lse = np.full((d, spec.batch, spec.num_q_heads), np.nan)
+    out = np.full((d, spec.batch, n * hq, spec.v_dim), np.nan)
+    lse = np.full((d, spec.batch, n * hq), np.nan)
     for b in bsel:
         q = query(w, b)
+        qp = query_positions(w, b) if q_pos is None else [int(q_pos[b]) + t for t in range(n)]
         for r in range(d):
             pos = shard_positions(int(w.seq_lens[b]), spec.block_size, d, r, ownership)
             k, v = sequence_kv(w, b, pos)
-            out[r, b], lse[r, b] = attend(q, k, v, spec.softmax_scale)
+            for t, p in enumerate(qp):
+                rows = slice(t * hq, (t + 1) * hq)
+                keep = pos <= p
+                out[r, b, rows], lse[r, b, rows] = attend(q[rows], k[keep], v[keep],
+                                                          spec.softmax_scale)
     return out, lse
 
 
@@ -173,6 +203,8 @@ def ml_partials(w, num_shards=None, batch_indices=None):
     m = -inf, l = 0, O = 0.
     """
     spec = w.spec
+    if spec.q_len != 1:
+        raise ValueError("the (m, l) form here covers single-token decode")
     d = spec.num_shards if num_shards is None else num_shards
     bsel = range(spec.batch) if batch_indices is None else batch_indices
     hq, hkv = spec.num_q_heads, spec.num_kv_heads

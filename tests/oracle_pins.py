@@ -28,7 +28,7 @@ def _golden(name):
 
 # ----------------------------------------------------------------- fake workloads
 def fake_workload(kind, seq_lens, *, hq, hkv=1, dqk, dv, bs, kv_dtype="f32", scale=None,
-                  seed=0):
+                  seed=0, q_len=1):
     """A small paged workload built here, independent of the workloads module.
 
     The contiguous K/V (or latent) of each sequence is drawn first and then
@@ -71,7 +71,7 @@ def fake_workload(kind, seq_lens, *, hq, hkv=1, dqk, dv, bs, kv_dtype="f32", sca
         if v_pool is not None:
             v_bits = v_pool.astype(np.float32)
             v_val = v_bits.astype(np.float64)
-    q32 = rng.standard_normal((batch, hq, dqk)).astype(np.float32)
+    q32 = rng.standard_normal((batch, q_len * hq, dqk)).astype(np.float32)
     if kv_dtype in ("bf16", "fp8"):
         q_t = torch.from_numpy(q32).to(torch.bfloat16)
         q_store = q_t.view(torch.int16).numpy().view(np.uint16)
@@ -97,7 +97,7 @@ def fake_workload(kind, seq_lens, *, hq, hkv=1, dqk, dv, bs, kv_dtype="f32", sca
                            qk_dim=dqk, v_dim=dv, block_size=bs, kv_dtype=kv_dtype,
                            q_dtype=q_dtype,
                            softmax_scale=(1.0 / math.sqrt(dqk)) if scale is None else scale,
-                           num_shards=1)
+                           num_shards=1, q_len=q_len)
     w = SimpleNamespace(spec=spec, seq_lens=lens, block_table=table, q=q_store,
                         k_cache=k_bits, v_cache=(v_bits if kind == "gqa" else None),
                         kv_scale=(sigma_pool.astype(np.float32) if kv_dtype == "fp8" else None))
@@ -458,6 +458,66 @@ def check_merge_invariants(O):
     assert np.all(zo == 0) and np.all(zl == -np.inf)
 
 
+# ----------------------------------------------------------------- multi-token decode
+def _sdpa_causal(q, k, v, scale, n):
+    """torch SDPA (float64) of n query tokens [n, Hq, d] against L positions with the
+    bottom-right causal mask built by torch.tril: query t sees p <= t + L - n."""
+    L = k.shape[0]
+    hq, hkv = q.shape[1], k.shape[1]
+    qt = torch.from_numpy(np.ascontiguousarray(q)).permute(1, 0, 2)[None].contiguous()
+    kt = torch.from_numpy(np.ascontiguousarray(k)).permute(1, 0, 2)[None].contiguous()
+    vt = torch.from_numpy(np.ascontiguousarray(v)).permute(1, 0, 2)[None].contiguous()
+    mask = torch.ones((n, L), dtype=torch.bool).tril(diagonal=L - n)
+    seen = mask.any(dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=mask, scale=scale, enable_gqa=(hq != hkv))[0]  # [Hq, n, dv]
+    krep = kt[0].repeat_interleave(hq // hkv, dim=0)  # [Hq, L, d]
+    s = scale * torch.matmul(qt[0], krep.transpose(1, 2).contiguous())  # [Hq, n, L]
+    s = s.masked_fill(~mask[None], float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)  # [Hq, n]
+    o = torch.where(seen[None, :, None], o, torch.zeros_like(o))
+    return o.permute(1, 0, 2).numpy(), lse.permute(1, 0).numpy()
+
+
+def check_mtp_causal_sdpa(O):
+    for kind, dtype, hq, hkv, n in (("mla", "bf16", 4, 1, 3), ("gqa", "f32", 4, 2, 4),
+                                    ("mla", "fp8", 2, 1, 2)):
+        dqk, dv = (24, 16) if kind == "mla" else (16, 16)
+        w, cont = fake_workload(kind, [40, 5, 9, 17], hq=hq, hkv=hkv, dqk=dqk, dv=dv, bs=4,
+                                kv_dtype=dtype, seed=41, q_len=n)
+        o, lse = O.decode_reference(w)
+        for b, (q, k, v) in enumerate(cont):
+            os_, ls = _sdpa_causal(q.reshape(n, hq, dqk), k, v, w.spec.softmax_scale, n)
+            _close(o[b].reshape(n, hq, dv), os_, 1e-11, 1e-12)
+            _close(lse[b].reshape(n, hq), ls, 1e-12, 1e-12)
+
+
+def check_mtp_closed_form(O):
+    """L == q_len: query t sees exactly positions 0..t; query 0 sees one token, so its
+    output is that token's value and its LSE is that token's score."""
+    w, cont = fake_workload("gqa", [3, 1], hq=2, hkv=1, dqk=8, dv=8, bs=2, seed=43, q_len=3)
+    o, lse = O.decode_reference(w)
+    q, k, v = cont[0]
+    _close(o[0, 0:2], np.repeat(v[0], 2, axis=0), 1e-15, 0)
+    _close(lse[0, 0:2], w.spec.softmax_scale * (q[0:2] @ k[0, 0]), 1e-14, 0)
+    # Sequence of one cached token with three queries: only query 2 sees it.
+    assert np.all(lse[1, 0:4] == -np.inf) and np.all(o[1, 0:4] == 0)
+    _close(o[1, 4:6], np.repeat(cont[1][2][0], 2, axis=0), 1e-15, 0)
+
+
+def check_mtp_shard_merge(O):
+    for kind, lens in (("mla", [40, 5, 2, 17, 64]), ("gqa", [33, 8, 1, 20])):
+        dqk, dv, hkv = (24, 16, 1) if kind == "mla" else (16, 16, 2)
+        w, _ = fake_workload(kind, lens, hq=4, hkv=hkv, dqk=dqk, dv=dv, bs=4,
+                             kv_dtype="bf16" if kind == "mla" else "f32", seed=44, q_len=3)
+        o_ref, lse_ref = O.decode_reference(w)
+        for d in range(1, 7):
+            op, lp = O.shard_partials(w, d)
+            o, lse = O.lse_merge(op, lp)
+            _close(o, o_ref, 1e-12, 1e-13)
+            _close(lse, lse_ref, 1e-12, 1e-13)
+
+
 # ----------------------------------------------------------------- fp8 encode and KV append
 def _nearest_code_bruteforce(y, codes, vals):
     """Nearest finite code to y by search; ties to the even code (mantissa bit 0)."""
@@ -577,6 +637,9 @@ ALL_CHECKS = [
     check_fp8_rows,
     check_shard_merge_equals_unsharded,
     check_merge_invariants,
+    check_mtp_causal_sdpa,
+    check_mtp_closed_form,
+    check_mtp_shard_merge,
     check_e4m3_encoder,
     check_quantize_token,
     check_kv_append_bruteforce,

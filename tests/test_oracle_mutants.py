@@ -45,6 +45,12 @@ MUTANTS = [
     ("attention.py", "if owner_of_block(j, num_shards, ownership, nb) == shard:",
      "if owner_of_block(j, num_shards, ownership, nb) == (shard + 1) % num_shards:",
      "shard tokens shifted"),
+    ("attention.py", "seen = max(0, p + 1)", "seen = max(0, p)", "causal mask hides the query's own position"),
+    ("attention.py", "keep = pos <= p", "keep = pos < p", "shard causal mask off by one"),
+    ("attention.py", "return [int(w.seq_lens[b]) - n + t for t in range(n)]",
+     "return [int(w.seq_lens[b]) - 1 - t for t in range(n)]", "query positions reversed"),
+    ("attention.py", "rows = slice(t * hq, (t + 1) * hq)\n            seen",
+     "rows = slice(t, n * hq, n)\n            seen", "queries read head-major"),
     ("paged.py", "return j // chunk_of(nb, num_shards)",
      "return min(num_shards - 1, j * num_shards // max(nb, 1))", "contiguous chunks balanced differently"),
     ("paged.py", "return j % num_shards", "return (j + 1) % num_shards", "owner off by one"),

@@ -69,6 +69,7 @@ class Spec:
     softmax_scale: float
     seed: int
     len_div: int = 1  # divides every length (scaled-down twin of a workload)
+    q_len: int = 1  # query tokens per sequence (multi-token decode when > 1)
 
     @property
     def q_dtype(self) -> str:
@@ -142,7 +143,8 @@ class Workload:
     """Host-side arrays for one workload.
 
     Layouts (all C-contiguous):
-      q           [B, Hq, qk_dim]             float32, or uint16 bf16 bit patterns
+      q           [B, q_len * Hq, qk_dim]     float32, or uint16 bf16 bit patterns
+                  (token-major: row t * Hq + h is head h of query token t)
       k_cache     gqa: [num_blocks, bs, Hkv, qk_dim]; mla: latent [num_blocks, bs, qk_dim]
       v_cache     gqa: [num_blocks, bs, Hkv, v_dim];  mla: None (V is latent[..., :v_dim])
       kv_scale    fp8 only: float32 [num_blocks, bs], one scale per cached token
@@ -255,7 +257,7 @@ def _build(spec: Spec, lens: np.ndarray) -> Workload:
     s = spec.seed
     table, num_blocks = build_block_table(lens, spec.block_size, s)
     q32 = np.random.default_rng([s, _S_Q]).standard_normal(
-        (spec.batch, spec.num_q_heads, spec.qk_dim), dtype=np.float32)
+        (spec.batch, spec.q_len * spec.num_q_heads, spec.qk_dim), dtype=np.float32)
     q = _encode(q32, spec.q_dtype)
     bs = spec.block_size
     scale = None
@@ -281,12 +283,13 @@ def make(spec, seed: Optional[int] = None) -> Workload:
 
 def custom(kind: str, seq_lens, *, num_q_heads: int, num_kv_heads: int = 1, qk_dim: int,
            v_dim: int, block_size: int, num_shards: int, kv_dtype: str, softmax_scale=None,
-           seed: int = 0, name: str = "custom") -> Workload:
+           seed: int = 0, name: str = "custom", q_len: int = 1) -> Workload:
     """A workload with explicit per-sequence lengths (edge cases, ragged tails)."""
     lens = np.asarray(seq_lens, dtype=np.int32).reshape(-1)
     spec = Spec(name, kind, len(lens), num_q_heads, num_kv_heads, qk_dim, v_dim, block_size,
                 num_shards, kv_dtype, "explicit",
-                softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(qk_dim), seed)
+                softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(qk_dim), seed,
+                q_len=q_len)
     return _build(spec, lens)
 
 

@@ -141,9 +141,35 @@ def components(dcp, desc, dev, w, ws, iters: int = 20):
         return {"shard": r, "ms": round(shard_ms[r], 4), "kv_bytes": b,
                 "GBps": round(b / (shard_ms[r] * 1e-3) / 1e9, 1)}
 
+    # A decode step's cache maintenance: one new token per sequence, written at
+    # the last position each table row maps, into a scratch pool of one block
+    # per sequence (so the workload's cache stays as generated), and the
+    # incremental table update from L - 1 to L tokens.
+    B, bs = spec.batch, spec.block_size
+    kind_rows = (B, spec.num_kv_heads, spec.qk_dim) if spec.kind == "gqa" else (B, spec.qk_dim)
+    new_dt = torch.float32 if spec.kv_dtype == "f32" else torch.bfloat16
+    k_new = torch.randn(kind_rows, device="cuda").to(new_dt)
+    v_new = (torch.randn((B, spec.num_kv_heads, spec.v_dim), device="cuda").to(new_dt)
+             if spec.kind == "gqa" else None)
+    pool_k = torch.empty((B,) + tuple(dev.k_cache.shape[1:]), dtype=dev.k_cache.dtype, device="cuda")
+    pool_v = torch.empty_like(pool_k) if dev.v_cache is not None else None
+    pool_s = (torch.empty((B, bs), dtype=torch.float32, device="cuda")
+              if dev.kv_scale is not None else None)
+    scratch_table = torch.arange(B, dtype=torch.int32, device="cuda")[:, None].expand(
+        B, dev.block_table.shape[1]).contiguous()
+    sdesc = dcp.make_desc(desc.kv_kind, dev.q, pool_k, scratch_table, num_shards=D,
+                          v_dim=spec.v_dim, softmax_scale=spec.softmax_scale)
+    pos = (dev.seq_lens - 1).clamp(min=0).to(torch.int32).contiguous()
+    append_ms = timed(lambda: dcp.kv_append(sdesc, pos, k_new, v_new, scratch_table, pool_k,
+                                             pool_v, pool_s))
+    lt_u, ll_u = lt.clone(), ll.clone()
+    upd_ms = timed(lambda: dcp.block_remap_update(dev.block_table, pos, dev.seq_lens,
+                                                  spec.block_size, D, lt_u, ll_u))
     return {
         "note": "per call, wall time of back-to-back calls; each dcp_decode_partial includes its own plan and piece merge",
         "block_remap_ms": round(remap_ms, 4),
+        "block_remap_update_ms": round(upd_ms, 4),
+        "kv_append_ms": round(append_ms, 4),
         "decode_partial_shard0": shard(0),
         "decode_partial_slowest": shard(slow),
         "lse_merge": {"partials": D, "ms": round(merge_ms, 4), "bytes": merge_bytes,

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI, without the ``dcp_`` prefix):
   kv_append          a decode step's KV write into the owning block (fp8: quantised on write)
   workspace_size     device workspace bytes for a descriptor
   decode_partial     one shard's partial output and log-sum-exp
+  decode_partial_mtp the same for q_len query tokens per sequence (causal by global position)
   lse_merge          merge of D partials: O = sum_i exp(LSE_i) / sum_j exp(LSE_j) * O_i
   decode_all_shards  all D shards of one layer plus the merge, fused
 """
@@ -27,7 +28,7 @@ import torch
 __all__ = [
     "AttnDesc", "DcpError", "LibraryMissing", "F32", "BF16", "FP8_E4M3", "KV_SEPARATE",
     "KV_LATENT", "OWN_INTERLEAVED", "OWN_CONTIGUOUS", "library_path", "lib", "make_desc", "block_remap", "block_remap_update", "kv_append", "workspace_size",
-    "decode_partial", "lse_merge", "decode_all_shards", "status_str", "version",
+    "decode_partial", "decode_partial_mtp", "lse_merge", "decode_all_shards", "status_str", "version",
 ]
 
 _LIB_PATH = Path(__file__).resolve().with_name("libdcp.so")
@@ -74,6 +75,7 @@ class AttnDesc(ctypes.Structure):
         ("kv_block_stride", ctypes.c_int64),
         ("kv_token_stride", ctypes.c_int64),
         ("kv_head_stride", ctypes.c_int64),
+        ("q_len", ctypes.c_int32),
     ]
 
 
@@ -108,6 +110,9 @@ def lib():
         L.dcp_decode_partial.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P,
                                          _P, ctypes.c_size_t, _P]
         L.dcp_decode_partial.restype = _I
+        L.dcp_decode_partial_mtp.argtypes = [ctypes.POINTER(AttnDesc), _I, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.dcp_decode_partial_mtp.restype = _I
         L.dcp_lse_merge.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]
         L.dcp_lse_merge.restype = _I
         L.dcp_decode_all_shards.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P,
@@ -174,13 +179,21 @@ def _code(t: torch.Tensor) -> int:
 
 def make_desc(kind: int, q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor, *,
               num_shards: int, v_dim: Optional[int] = None, softmax_scale: Optional[float] = None,
-              max_seq_len: Optional[int] = None, out_dtype: int = F32) -> AttnDesc:
-    """Descriptor for q [B, Hq, qk_dim] and a cache laid out as
-    [num_blocks, block_size, Hkv, dim] (KV_SEPARATE) or [num_blocks, block_size, qk_dim]
+              max_seq_len: Optional[int] = None, out_dtype: int = F32,
+              q_len: int = 1) -> AttnDesc:
+    """Descriptor for q [B, q_len * Hq, qk_dim] (or [B, q_len, Hq, qk_dim]) and a cache laid
+    out as [num_blocks, block_size, Hkv, dim] (KV_SEPARATE) or [num_blocks, block_size, qk_dim]
     (KV_LATENT); strides are taken from ``k_cache``."""
     d = AttnDesc()
     d.struct_size = ctypes.sizeof(AttnDesc)
-    d.batch, d.num_q_heads, d.qk_dim = (int(x) for x in q.shape)
+    if q.dim() == 4:
+        d.batch, q_len, d.num_q_heads, d.qk_dim = (int(x) for x in q.shape)
+    else:
+        d.batch, rows, d.qk_dim = (int(x) for x in q.shape)
+        if rows % q_len:
+            raise DcpValueError(DCP_ERR_INVALID_ARG, f"{rows} query rows are not {q_len} tokens")
+        d.num_q_heads = rows // q_len
+    d.q_len = int(q_len)
     if k_cache.numel() == 0:  # an empty pool reports zero strides; use contiguous ones
         strides, acc = [], 1
         for n in reversed(k_cache.shape):
@@ -303,16 +316,45 @@ def decode_partial(desc: AttnDesc, q, k_cache, v_cache, kv_scale, local_block_ta
     dev = q.device
     if workspace is None:
         workspace = alloc_workspace(desc, dev)
+    rows = _rows(desc)
     if o_partial is None:
-        o_partial = torch.empty((desc.batch, desc.num_q_heads, desc.v_dim), dtype=torch.float32,
-                                device=dev)
+        o_partial = torch.empty((desc.batch, rows, desc.v_dim), dtype=torch.float32, device=dev)
     if lse_partial is None:
-        lse_partial = torch.empty((desc.batch, desc.num_q_heads), dtype=torch.float32, device=dev)
+        lse_partial = torch.empty((desc.batch, rows), dtype=torch.float32, device=dev)
     _check(lib().dcp_decode_partial(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(kv_scale), _ptr(local_block_table),
                                     _ptr(local_seq_lens), _ptr(o_partial), _ptr(lse_partial),
                                     _ptr(workspace), workspace.numel(), _stream(dev)))
     return o_partial, lse_partial
+
+
+def decode_partial_mtp(desc: AttnDesc, shard: int, q_pos: torch.Tensor, q, k_cache, v_cache,
+                       kv_scale, local_block_table, local_seq_lens,
+                       workspace: Optional[torch.Tensor] = None,
+                       o_partial: Optional[torch.Tensor] = None,
+                       lse_partial: Optional[torch.Tensor] = None):
+    """One shard's multi-token partial: query t of sequence b at global position
+    q_pos[b] + t sees that shard's positions up to its own. Returns
+    (O_r [B, q_len * Hq, v_dim] fp32, LSE_r [B, q_len * Hq] fp32)."""
+    dev = q.device
+    if workspace is None:
+        workspace = alloc_workspace(desc, dev)
+    rows = _rows(desc)
+    if o_partial is None:
+        o_partial = torch.empty((desc.batch, rows, desc.v_dim), dtype=torch.float32, device=dev)
+    if lse_partial is None:
+        lse_partial = torch.empty((desc.batch, rows), dtype=torch.float32, device=dev)
+    _need(q_pos, torch.int32, desc.batch)
+    _check(lib().dcp_decode_partial_mtp(ctypes.byref(desc), int(shard), _ptr(q_pos), _ptr(q),
+                                        _ptr(k_cache), _ptr(v_cache), _ptr(kv_scale),
+                                        _ptr(local_block_table), _ptr(local_seq_lens),
+                                        _ptr(o_partial), _ptr(lse_partial), _ptr(workspace),
+                                        workspace.numel(), _stream(dev)))
+    return o_partial, lse_partial
+
+
+def _rows(desc: AttnDesc) -> int:
+    return max(1, int(desc.q_len)) * int(desc.num_q_heads)
 
 
 def lse_merge(o_partials: torch.Tensor, lse_partials: torch.Tensor,
@@ -341,11 +383,12 @@ def decode_all_shards(desc: AttnDesc, q, k_cache, v_cache, kv_scale, block_table
     dev = q.device
     if workspace is None:
         workspace = alloc_workspace(desc, dev)
+    rows = _rows(desc)
     if out is None:
         dt = torch.float32 if desc.out_dtype == F32 else torch.bfloat16
-        out = torch.empty((desc.batch, desc.num_q_heads, desc.v_dim), dtype=dt, device=dev)
+        out = torch.empty((desc.batch, rows, desc.v_dim), dtype=dt, device=dev)
     if lse_out is None and want_lse:
-        lse_out = torch.empty((desc.batch, desc.num_q_heads), dtype=torch.float32, device=dev)
+        lse_out = torch.empty((desc.batch, rows), dtype=torch.float32, device=dev)
     if attn_events is None:
         _check(lib().dcp_decode_all_shards(ctypes.byref(desc), _ptr(q), _ptr(k_cache),
                                            _ptr(v_cache), _ptr(kv_scale), _ptr(block_table),

@@ -18,7 +18,9 @@ bool valid_dtype(int t) { return t == DCP_F32 || t == DCP_BF16 || t == DCP_FP8_E
 
 // Shape and type checks shared by every attention entry point.
 dcp_status_t check_desc(const dcp_attn_desc_t* d) {
-  if (!d || d->struct_size < sizeof(dcp_attn_desc_t)) return DCP_ERR_INVALID_ARG;
+  if (!d || d->struct_size < DCP_ATTN_DESC_MIN_SIZE) return DCP_ERR_INVALID_ARG;
+  if (d->struct_size >= sizeof(dcp_attn_desc_t) && (d->q_len < 0 || d->q_len > 64))
+    return DCP_ERR_INVALID_ARG;
   if (d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->qk_dim < 1 ||
       d->v_dim < 1 || d->block_size < 1 || d->max_blocks_per_seq < 1 || d->num_shards < 1 ||
       d->max_seq_len < 0 || d->num_cache_blocks < 0)
@@ -65,31 +67,58 @@ dcp_status_t check_tensors(const dcp_attn_desc_t* d, const void* q, const void* 
 }
 
 dcp_status_t run_attention(const dcp_attn_desc_t* d, const void* q, const void* k, const void* v,
-                           const float* kv_scale, const SegMap& map, int S, void* out,
-                           dcp_dtype_t out_dtype, float* lse_out, void* workspace,
+                           const float* kv_scale, const SegMap& map, int S, const Causal& cz,
+                           void* out, dcp_dtype_t out_dtype, float* lse_out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream,
                            hipEvent_t attn_begin = nullptr, hipEvent_t attn_end = nullptr) {
   const int G = groups_for(d);
-  const size_t need = workspace_bytes_for(S, G, d->batch, d->num_q_heads, d->v_dim);
+  const int rows = desc_rows(d);
+  const size_t need = workspace_bytes_for(S, G, d->batch, rows, d->v_dim);
   SegMap m = map;
   // No cache blocks: every block id is unusable, so every sequence is empty.
   if (d->num_cache_blocks == 0) m.width = 0;
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
-  WorkspaceView ws = carve_workspace(workspace, S, G, d->batch, d->num_q_heads, d->v_dim);
+  WorkspaceView ws = carve_workspace(workspace, S, G, d->batch, rows, d->v_dim);
   // Fixed work per piece of a segment, in blocks (about 128 tokens' worth).
   const int seg_cost = (128 + d->block_size - 1) / d->block_size;
   const bool seq_pieces = d->kv_kind == DCP_KV_LATENT && mla_sequence_pieces(d);
-  if (launch_plan(m, S, G, seg_cost, d->num_q_heads, seq_pieces, ws, stream) != hipSuccess)
+  if (launch_plan(m, S, G, seg_cost, rows, seq_pieces, ws, stream) != hipSuccess)
     return DCP_ERR_HIP;
-  AttnLaunch L{d, q, k, v, kv_scale, m, S, ws};
+  AttnLaunch L{d, q, k, v, kv_scale, m, S, ws, cz};
   if (attn_begin && hipEventRecord(attn_begin, stream) != hipSuccess) return DCP_ERR_HIP;
   hipError_t err = d->kv_kind == DCP_KV_LATENT ? launch_mla(L, stream) : launch_gqa(L, stream);
   if (err != hipSuccess) return DCP_ERR_HIP;
   if (attn_end && hipEventRecord(attn_end, stream) != hipSuccess) return DCP_ERR_HIP;
-  if (launch_merge_pieces(m, ws, G, d->num_q_heads, d->v_dim, out, out_dtype, lse_out, stream) !=
+  if (launch_merge_pieces(m, ws, G, rows, d->v_dim, out, out_dtype, lse_out, stream) !=
       hipSuccess)
     return DCP_ERR_HIP;
   return DCP_OK;
+}
+
+// One shard's partial over its local table. q_pos null: single-token decode
+// (no mask); else the causal multi-token form with global positions
+// shard + D * (local block) .
+dcp_status_t shard_partial(const dcp_attn_desc_t* d, int shard, const int32_t* q_pos,
+                           const void* q, const void* k_cache, const void* v_cache,
+                           const float* kv_scale, const int32_t* local_block_table,
+                           const int32_t* local_seq_lens, float* o_partial, float* lse_partial,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dcp_status_t st;
+  if ((st = check_tensors(d, q, k_cache, v_cache, kv_scale)) != DCP_OK) return st;
+  if (!local_block_table || !local_seq_lens || !o_partial || !lse_partial)
+    return DCP_ERR_INVALID_ARG;
+  if (!aligned(o_partial, 16)) return DCP_ERR_INVALID_ARG;
+  if (d->batch == 0) return DCP_OK;
+  SegMap map;
+  map.table = local_block_table;
+  map.lens = local_seq_lens;
+  map.width = (d->max_blocks_per_seq + d->num_shards - 1) / d->num_shards;
+  map.D = 1;
+  map.bs = d->block_size;
+  map.batch = d->batch;
+  Causal cz{q_pos, q_pos ? desc_q_len(d) : 1, d->num_q_heads, shard, d->num_shards};
+  return run_attention(d, q, k_cache, v_cache, kv_scale, map, d->batch, cz, o_partial, DCP_F32,
+                       lse_partial, workspace, workspace_bytes, stream);
 }
 
 }  // namespace
@@ -113,8 +142,8 @@ size_t dcp_workspace_size(const dcp_attn_desc_t* d) {
   if (check_desc(d) != DCP_OK) return 0;
   const int G = groups_for(d);
   const int S_all = d->batch * d->num_shards;
-  const size_t a = workspace_bytes_for(S_all, G, d->batch, d->num_q_heads, d->v_dim);
-  const size_t b = workspace_bytes_for(d->batch, G, d->batch, d->num_q_heads, d->v_dim);
+  const size_t a = workspace_bytes_for(S_all, G, d->batch, desc_rows(d), d->v_dim);
+  const size_t b = workspace_bytes_for(d->batch, G, d->batch, desc_rows(d), d->v_dim);
   return a > b ? a : b;
 }
 
@@ -196,20 +225,22 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* d, const void* q, const v
                                 size_t workspace_bytes, hipStream_t stream) {
   dcp_status_t st = check_desc(d);
   if (st != DCP_OK) return st;
-  if ((st = check_tensors(d, q, k_cache, v_cache, kv_scale)) != DCP_OK) return st;
-  if (!local_block_table || !local_seq_lens || !o_partial || !lse_partial)
-    return DCP_ERR_INVALID_ARG;
-  if (!aligned(o_partial, 16)) return DCP_ERR_INVALID_ARG;
-  if (d->batch == 0) return DCP_OK;
-  SegMap map;
-  map.table = local_block_table;
-  map.lens = local_seq_lens;
-  map.width = (d->max_blocks_per_seq + d->num_shards - 1) / d->num_shards;
-  map.D = 1;
-  map.bs = d->block_size;
-  map.batch = d->batch;
-  return run_attention(d, q, k_cache, v_cache, kv_scale, map, d->batch, o_partial, DCP_F32,
-                       lse_partial, workspace, workspace_bytes, stream);
+  if (desc_q_len(d) > 1) return DCP_ERR_INVALID_ARG;
+  return shard_partial(d, 0, nullptr, q, k_cache, v_cache, kv_scale, local_block_table,
+                       local_seq_lens, o_partial, lse_partial, workspace, workspace_bytes, stream);
+}
+
+dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* d, int32_t shard, const int32_t* q_pos,
+                                    const void* q, const void* k_cache, const void* v_cache,
+                                    const float* kv_scale, const int32_t* local_block_table,
+                                    const int32_t* local_seq_lens, float* o_partial,
+                                    float* lse_partial, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  dcp_status_t st = check_desc(d);
+  if (st != DCP_OK) return st;
+  if (shard < 0 || shard >= d->num_shards || !q_pos) return DCP_ERR_INVALID_ARG;
+  return shard_partial(d, shard, q_pos, q, k_cache, v_cache, kv_scale, local_block_table,
+                       local_seq_lens, o_partial, lse_partial, workspace, workspace_bytes, stream);
 }
 
 dcp_status_t dcp_lse_merge(const float* o_partials, const float* lse_partials,
@@ -258,7 +289,8 @@ dcp_status_t dcp_decode_all_shards_timed(const dcp_attn_desc_t* d, const void* q
   map.D = d->num_shards;
   map.bs = d->block_size;
   map.batch = d->batch;
-  return run_attention(d, q, k_cache, v_cache, kv_scale, map, d->batch * d->num_shards, out,
+  const Causal cz{nullptr, desc_q_len(d), d->num_q_heads, 0, 1};
+  return run_attention(d, q, k_cache, v_cache, kv_scale, map, d->batch * d->num_shards, cz, out,
                        d->out_dtype, lse_out, workspace, workspace_bytes, stream, attn_begin,
                        attn_end);
 }

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "dcp.h"
@@ -209,6 +210,27 @@ hipError_t launch_kv_append(const dcp_attn_desc_t* d, int n_tokens, const int32_
                             dcp_dtype_t new_dtype, int shard, const int32_t* table, void* k_cache,
                             void* v_cache, float* kv_scale, hipStream_t stream);
 
+// Multi-token decode. A sequence carries q_len query tokens (rows t * hq + h
+// of q, partials and output); query t of sequence b sits at position
+// q_pos[b] + t (q_pos null: seq_tokens - q_len) and sees the positions up to
+// its own. Table column col of the segment map holds global block
+// pos_r + pos_D * col (fused path: 0 + 1 * col; one shard's local table:
+// shard + D * col), which gives every cached token its global position.
+struct Causal {
+  const int32_t* q_pos;
+  int q_len;  // 1: single-token decode, no mask
+  int hq;     // query heads per token
+  int pos_r, pos_D;
+};
+
+__device__ __forceinline__ long long first_query_pos(const Causal& c, const SegMap& m, int b) {
+  return c.q_pos ? static_cast<long long>(c.q_pos[b])
+                 : static_cast<long long>(seq_tokens(m, b)) - c.q_len;
+}
+__device__ __forceinline__ long long global_pos(const Causal& c, int col, int bs, int slot) {
+  return (static_cast<long long>(c.pos_r) + static_cast<long long>(c.pos_D) * col) * bs + slot;
+}
+
 struct AttnLaunch {
   const dcp_attn_desc_t* desc;
   const void* q;
@@ -218,7 +240,16 @@ struct AttnLaunch {
   SegMap map;
   int S;
   WorkspaceView ws;
+  Causal cz;
 };
+
+// Query tokens per sequence and query rows per sequence of a descriptor (a
+// descriptor whose struct_size ends before q_len has one query token).
+inline int desc_q_len(const dcp_attn_desc_t* d) {
+  const bool has = d->struct_size >= offsetof(dcp_attn_desc_t, q_len) + sizeof(int32_t);
+  return has && d->q_len > 1 ? d->q_len : 1;
+}
+inline int desc_rows(const dcp_attn_desc_t* d) { return desc_q_len(d) * d->num_q_heads; }
 
 // Work groups per launch for each kernel family (a property of the kernel, not
 // of the device, so workspace sizes are pure functions of the descriptor).

@@ -38,12 +38,23 @@ struct GqaArgs {
   float* ws_lse;
   long long block_stride_b, token_stride_b, head_stride_b;  // bytes
   int S;
-  int G;      // ranges (work groups per KV head)
+  int G;      // ranges (work groups per KV head and column tile)
   int ncb;
-  int Hq;
+  int Hq;     // query rows per sequence (q_len * heads per token)
   int group;  // query heads per KV head
+  int cols;   // query rows per KV head: group * q_len, in tiles of 16
+  int ctiles;
   float scale_log2;
+  Causal cz;
+  bool causal;
 };
+
+// Column c of a KV head's query rows: token c / group, head c % group of that
+// KV head's group; its row in q and in the partials is token * Hq_tok + head.
+__device__ __forceinline__ int gqa_row(const GqaArgs& a, int kvh, int c) {
+  const int t = c / a.group;
+  return t * a.cz.hq + kvh * a.group + (c - t * a.group);
+}
 
 // (Through the builtin, so the compiler's own wait insertion sees it; the empty
 // asm keeps memory accesses from moving across it.)
@@ -75,15 +86,19 @@ __global__ __launch_bounds__(64) void gqa_bf16_kernel(GqaArgs a) {
 
   const int lane = threadIdx.x;
   const int q4 = lane >> 4, l16 = lane & 15;
-  const int kvh = blockIdx.y;
+  const int kvh = blockIdx.y / a.ctiles;
+  const int ct = blockIdx.y - kvh * a.ctiles;
   const int g = xcd_logical_group(blockIdx.x, a.G);
   int pos = a.wg_start[g];
   const int end = a.wg_start[g + 1];
   if (pos >= end) return;
   int s = find_segment(a.seg_off, a.S, pos);
   const int bs = a.map.bs;
-  const bool head_ok = l16 < a.group;
-  const int h = kvh * a.group + (head_ok ? l16 : 0);
+  // This lane's query row: column 16ct + l16 of the KV head's (token, head) rows.
+  const int col_q = 16 * ct + l16;
+  const bool head_ok = col_q < a.cols;
+  const int h = gqa_row(a, kvh, head_ok ? col_q : 0);
+  const int t_q = (head_ok ? col_q : 0) / a.group;  // its query token
 
   int a_off0[kKSteps], a_off1[kKSteps];
 #pragma unroll
@@ -107,6 +122,7 @@ __global__ __launch_bounds__(64) void gqa_bf16_kernel(GqaArgs a) {
     const Piece p = make_piece(a.map, s, pos - seg_a, pe - seg_a);
     const int b = p.b;
     const int32_t* trow = a.map.table + static_cast<size_t>(b) * a.map.width;
+    const long long qpos0 = a.causal ? first_query_pos(a.cz, a.map, b) : 0;
 
     bf16x8 qf[kKSteps];
     {
@@ -191,6 +207,19 @@ __global__ __launch_bounds__(64) void gqa_bf16_kernel(GqaArgs a) {
         x[i] = ((vm_k >> r0) & 1ull) ? s0[i] * a.scale_log2 : -INFINITY;
         x[4 + i] = ((vm_k >> r1) & 1ull) ? s1[i] * a.scale_log2 : -INFINITY;
       }
+      if (a.causal) {
+        // Multi-token decode: tile row r (lane r < 32 computes its global
+        // position) is visible to this lane's query token t_q if it lies at
+        // most t_q past the first query's position.
+        const int tau = k * kT + (lane & 31);
+        const long long e = global_pos(a.cz, piece_col(a.map, p, tau), bs, tau % bs) - qpos0;
+        const int ec = static_cast<int>(e < -1 ? -1 : (e > 127 ? 127 : e));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (__shfl(ec, 4 * q4 + i) > t_q) x[i] = -INFINITY;
+          if (__shfl(ec, 16 + 4 * q4 + i) > t_q) x[4 + i] = -INFINITY;
+        }
+      }
       float tmax = x[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
@@ -263,14 +292,16 @@ __global__ __launch_bounds__(64) void gqa_f32_kernel(GqaArgs a) {
   __shared__ int id_lds[kTok];
 
   const int lane = threadIdx.x;
-  const int kvh = blockIdx.y;
+  const int kvh = blockIdx.y / a.ctiles;
+  const int ct = blockIdx.y - kvh * a.ctiles;
   const int g = xcd_logical_group(blockIdx.x, a.G);
   int pos = a.wg_start[g];
   const int end = a.wg_start[g + 1];
   if (pos >= end) return;
   int s = find_segment(a.seg_off, a.S, pos);
   const int bs = a.map.bs;
-  const int G = a.group;
+  // Columns j < G of this wave: the KV head's query rows 16ct + j (token, head).
+  const int G = min(kMaxGroup, a.cols - 16 * ct);
 
   while (pos < end) {
     while (a.seg_off[s + 1] <= pos) ++s;
@@ -279,8 +310,10 @@ __global__ __launch_bounds__(64) void gqa_f32_kernel(GqaArgs a) {
     const Piece p = make_piece(a.map, s, pos - seg_a, pe - seg_a);
     const int b = p.b;
     const int32_t* trow = a.map.table + static_cast<size_t>(b) * a.map.width;
-    const float* qb = static_cast<const float*>(a.q) + (static_cast<size_t>(b) * a.Hq + kvh * G) * DH;
-    for (int i = lane; i < G * DH; i += 64) q_lds[i / DH][i % DH] = qb[i];
+    const float* qb = static_cast<const float*>(a.q) + static_cast<size_t>(b) * a.Hq * DH;
+    for (int i = lane; i < G * DH; i += 64)
+      q_lds[i / DH][i % DH] = qb[static_cast<size_t>(gqa_row(a, kvh, 16 * ct + i / DH)) * DH + i % DH];
+    const long long qpos0 = a.causal ? first_query_pos(a.cz, a.map, b) : 0;
     float m_run[kMaxGroup], l_run[kMaxGroup], acc[kMaxGroup][kCols];
 #pragma unroll
     for (int j = 0; j < kMaxGroup; ++j) {
@@ -296,6 +329,10 @@ __global__ __launch_bounds__(64) void gqa_f32_kernel(GqaArgs a) {
       if (tau < p.ntok) id = trow[piece_col(a.map, p, tau)];
       const bool ok = tau < p.ntok && id >= 0 && id < a.ncb;
       id_lds[lane] = ok ? id : -1;
+      // Multi-token decode: how far this token lies past the first query.
+      const long long e = a.causal && ok
+                              ? global_pos(a.cz, piece_col(a.map, p, tau), bs, tau % bs) - qpos0
+                              : -1;
       const float* krow = ok ? reinterpret_cast<const float*>(
                                    a.k + static_cast<long long>(id) * a.block_stride_b +
                                    static_cast<long long>(tau % bs) * a.token_stride_b +
@@ -307,7 +344,8 @@ __global__ __launch_bounds__(64) void gqa_f32_kernel(GqaArgs a) {
         float dot = 0.f;
         if (ok)
           for (int d = 0; d < DH; ++d) dot = fmaf(q_lds[j][d], krow[d], dot);
-        const float x = ok ? dot * a.scale_log2 : -INFINITY;
+        const bool seen = ok && e <= (16 * ct + j) / a.group;
+        const float x = seen ? dot * a.scale_log2 : -INFINITY;
         float tmax = x;
         for (int off = 32; off >= 1; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off));
         const float m_new = fmaxf(m_run[j], tmax);
@@ -347,7 +385,7 @@ __global__ __launch_bounds__(64) void gqa_f32_kernel(GqaArgs a) {
 #pragma unroll
     for (int j = 0; j < kMaxGroup; ++j) {
       if (j >= G) continue;
-      const int h = kvh * G + j;
+      const int h = gqa_row(a, kvh, 16 * ct + j);
       const float inv = l_run[j] > 0.f ? 1.f / l_run[j] : 0.f;
 #pragma unroll
       for (int c = 0; c < kCols; ++c) a.ws_o[(slot * a.Hq + h) * DH + lane + 64 * c] = acc[j][c] * inv;
@@ -396,10 +434,14 @@ hipError_t launch_gqa(const AttnLaunch& L, hipStream_t stream) {
   a.S = L.S;
   a.G = gqa_groups(d);
   a.ncb = d->num_cache_blocks;
-  a.Hq = d->num_q_heads;
+  a.Hq = desc_rows(d);
   a.group = d->num_q_heads / d->num_kv_heads;
+  a.cols = a.group * desc_q_len(d);
+  a.ctiles = (a.cols + 15) / 16;
   a.scale_log2 = d->softmax_scale * kLog2e;
-  const dim3 grid(a.G, d->num_kv_heads);
+  a.cz = L.cz;
+  a.causal = L.cz.q_len > 1 || L.cz.q_pos != nullptr;
+  const dim3 grid(a.G, d->num_kv_heads * a.ctiles);
   if (d->kv_dtype == DCP_BF16) {
     if (d->qk_dim == 128)
       hipLaunchKernelGGL(gqa_bf16_kernel<128>, grid, dim3(64), 0, stream, a);

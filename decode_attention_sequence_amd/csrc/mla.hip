@@ -91,8 +91,10 @@ struct MlaArgs {
   const char* zero;         // 16 zero bytes (workspace)
   int S;
   int ncb;
-  int Hq;
+  int Hq;   // query rows per sequence (q_len * heads per token)
   float scale_log2;
+  Causal cz;
+  bool causal;  // multi-token decode or explicit query positions: mask by position
 };
 
 template <int V>
@@ -370,6 +372,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
     const int pe = min(end, a.seg_off[s + 1]);
     const Piece p = make_piece(a.map, s, pos - seg_a, pe - seg_a);
     const int32_t* trow = a.map.table + static_cast<size_t>(p.b) * a.map.width;
+    const long long qpos0 = a.causal ? first_query_pos(a.cz, a.map, p.b) : 0;
 
     // Query fragments (B operand of S^T): head h_s, columns 32kk + 8q4 .. +7.
     typename E::vec qf[kKSteps];
@@ -416,6 +419,22 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
             ok = id >= 0 && id < a.ncb;
           }
           return __ballot(ok);
+        }
+      };
+
+      // Multi-token decode: rows of tile j visible to this wave's query token
+      // (its 16 heads belong to one token), by global position.
+      auto causal_rows = [&](int j) -> unsigned long long {
+        const int tau0 = j * kT;
+        const long long lim = qpos0 + (head0 + 16 * hg) / a.cz.hq;
+        if constexpr (BS32) {
+          const int col = p.r + a.map.D * (wb + tau0 / bs);
+          const long long vis = lim - global_pos(a.cz, col, bs, tau0 % bs) + 1;
+          return vis >= 32 ? 0xffffffffull : (vis <= 0 ? 0ull : ((1ull << vis) - 1));
+        } else {
+          const int tau = tau0 + (lane & 31);
+          const int col = p.r + a.map.D * (wb + tau / bs);
+          return __ballot(lane < 32 && global_pos(a.cz, col, bs, tau % bs) <= lim);
         }
       };
 
@@ -584,6 +603,9 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
         const f32x4 sv = sa + sb;
 
         // ---- softmax, part 1: this half's max per head, exchanged through LDS
+        // (vm_k, shared by every wave, also drives the cooperative zeroing; the
+        // causal rows differ per wave and only mask this wave's scores)
+        const unsigned long long vm_s = a.causal ? vm_k & causal_rows(k) : vm_k;
         float x[4], sig[4];
         f32x4 sc4 = {1.f, 1.f, 1.f, 1.f};
         if constexpr (FP8) {
@@ -598,7 +620,7 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * th + 4 * q4 + i;
           sig[i] = sc4[i];
-          x[i] = ((vm_k >> r) & 1ull) ? sv[i] * sig[i] * a.scale_log2 : -INFINITY;
+          x[i] = ((vm_s >> r) & 1ull) ? sv[i] * sig[i] * a.scale_log2 : -INFINITY;
         }
         float hmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         hmax = max_xor32(max_xor16(hmax));
@@ -1165,7 +1187,23 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         const int col = (pa[0] - b * D) + D * (pa[2] + tok / bs);
         int id = a.map.table[static_cast<size_t>(b) * a.map.width + col];
         if (!(id >= 0 && id < a.ncb)) id = -1;
-        const int nvalid = min(kT, pb[2] - tok);
+        int nvalid = min(kT, pb[2] - tok);
+        if (a.causal) {
+          // This work group's 64 rows belong to one query token t_q, which sees
+          // the positions up to q_pos + t_q; the tile's rows are consecutive
+          // positions of one block, so the visible rows are a prefix.
+          const int t_q = head0 / a.cz.hq;
+          const long long vis = first_query_pos(a.cz, a.map, b) + t_q -
+                                global_pos(a.cz, col, bs, tok % bs) + 1;
+          if (vis < nvalid) {
+            if (vis <= 0) {
+              id = -1;
+              nvalid = 1;
+            } else {
+              nvalid = static_cast<int>(vis);
+            }
+          }
+        }
         const unsigned y = static_cast<unsigned>((tok % bs) / kT) | (static_cast<unsigned>(nvalid - 1) << 8) |
                            (static_cast<unsigned>(p) << 16) |
                            ((j == 0 && (pb[3] & 1)) ? (1u << 30) : 0u) |
@@ -1709,19 +1747,23 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
 int mla_groups() { return kGroups; }
 
 bool mla_supported(const dcp_attn_desc_t* d) {
+  const int rows = desc_rows(d);
   return d->kv_kind == DCP_KV_LATENT && d->num_kv_heads == 1 && d->qk_dim == kQK &&
          d->v_dim == kV && d->q_dtype == DCP_BF16 &&
          (d->kv_dtype == DCP_BF16 || d->kv_dtype == DCP_FP8_E4M3) &&
-         (d->num_q_heads == 16 || d->num_q_heads == 32 || d->num_q_heads % 64 == 0) &&
-         d->num_q_heads <= 256;
+         (rows == 16 || rows == 32 || rows % 64 == 0) && rows <= 256 &&
+         (desc_q_len(d) == 1 || d->num_q_heads % 16 == 0);
 }
 
 // The producer/consumer kernel: groups of 64 heads, blocks of a multiple of 32
 // tokens (a tile then lies inside one block, and per-lane copy offsets,
 // row * token stride, fit in 32 bits).
+// Multi-token decode needs each 64-row head group to hold one query token.
 static bool use_pp(const dcp_attn_desc_t* d) {
   const long long elt = d->kv_dtype == DCP_BF16 ? 2 : 1;
-  return d->num_q_heads >= 64 && d->block_size % kT == 0 && d->kv_token_stride * elt * kT < (1ll << 30);
+  return desc_rows(d) >= 64 && d->block_size % kT == 0 &&
+         d->kv_token_stride * elt * kT < (1ll << 30) &&
+         (desc_q_len(d) == 1 || d->num_q_heads % 64 == 0);
 }
 
 bool mla_sequence_pieces(const dcp_attn_desc_t* d) {
@@ -1754,14 +1796,16 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   a.token_stride_b = d->kv_token_stride * elt;
   a.S = L.S;
   a.ncb = d->num_cache_blocks;
-  a.Hq = d->num_q_heads;
+  a.Hq = desc_rows(d);
   a.scale_log2 = d->softmax_scale * kLog2e;
+  a.cz = L.cz;
+  a.causal = L.cz.q_len > 1 || L.cz.q_pos != nullptr;
   const bool fp8 = d->kv_dtype == DCP_FP8_E4M3;
   // A tile of 32 tokens lies inside one block when blocks hold a multiple of
   // 32 tokens; per-lane copy offsets (row * token stride) then fit in 32 bits.
   const bool bs32 = d->block_size % kT == 0 && a.token_stride_b * kT < (1ll << 30);
-  const int heads = d->num_q_heads < 64 ? d->num_q_heads : 64;
-  const dim3 grid(kGroups, d->num_q_heads / heads);
+  const int heads = a.Hq < 64 ? a.Hq : 64;
+  const dim3 grid(kGroups, a.Hq / heads);
   if (use_pp(d)) {
     if (fp8) hipLaunchKernelGGL(mla_pp_kernel<true>, grid, dim3(512), 0, stream, a);
     else hipLaunchKernelGGL(mla_pp_kernel<false>, grid, dim3(512), 0, stream, a);

@@ -90,13 +90,25 @@ typedef struct {
   int64_t kv_block_stride;   /* elements between cache blocks */
   int64_t kv_token_stride;   /* elements between tokens of a block */
   int64_t kv_head_stride;    /* elements between KV heads of a token (0 for latent) */
+  int32_t q_len;             /* query tokens per sequence (0 or 1: single-token decode).
+                              * q_len > 1 is multi-token (draft / MTP) decode: the
+                              * queries are the last q_len cached positions of their
+                              * sequence and query t sees the positions up to its own.
+                              * q, out and partials then hold q_len * num_q_heads rows
+                              * per sequence, token-major (row t * num_q_heads + h).
+                              * A descriptor whose struct_size ends before this field
+                              * is read as q_len = 1. At most 64. */
 } dcp_attn_desc_t;
+
+/* Smallest struct_size accepted: descriptors from before the q_len field. */
+#define DCP_ATTN_DESC_MIN_SIZE offsetof(dcp_attn_desc_t, q_len)
 
 /* Supported kernels in this build:
  *   DCP_KV_SEPARATE: q_dtype == kv_dtype in {F32, BF16}; qk_dim == v_dim in
  *     {64, 128}; num_q_heads % num_kv_heads == 0.
  *   DCP_KV_LATENT: q BF16; kv BF16, or FP8_E4M3 with kv_scale; qk_dim 576,
- *     v_dim 512; num_q_heads 16, 32 or a multiple of 64 up to 256. With an
+ *     v_dim 512; q_len * num_q_heads 16, 32 or a multiple of 64 up to 256
+ *     (with q_len > 1, num_q_heads a multiple of 16). With an
  *     FP8 cache the products run in fp16: query values must lie inside the
  *     fp16 range (|q| <= 65504) and scales must not exceed 65504.
  * Cache rows (the qk_dim / v_dim values of one token and head) must start on
@@ -206,12 +218,37 @@ size_t dcp_workspace_size(const dcp_attn_desc_t* desc);
  *   local_seq_lens    [batch] int32, this shard's token counts
  *   o_partial         [batch, num_q_heads, v_dim] fp32 (out), normalised output
  *   lse_partial       [batch, num_q_heads] fp32 (out)
- * desc->num_shards only sizes the local table width here. */
+ * desc->num_shards only sizes the local table width here. desc->q_len must be
+ * at most 1 (multi-token decode needs global positions: dcp_decode_partial_mtp). */
 dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
                                 const void* v_cache, const float* kv_scale,
                                 const int32_t* local_block_table, const int32_t* local_seq_lens,
                                 float* o_partial, float* lse_partial, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/* One shard's partial for multi-token (draft / MTP) decode, which the DCP
+ * blog page lists as future work (section A5). Query t of sequence b sits at
+ * global position q_pos[b] + t and sees the positions p <= q_pos[b] + t
+ * among this shard's tokens. Local block i of this shard is global block
+ * shard + num_shards * i (interleaved ownership, "vLLM长序列推理优化" §2.2),
+ * which gives each local token its global position.
+ *   shard       this shard's index in [0, num_shards)
+ *   q_pos       [batch] int32 (device): position of query 0 of each sequence
+ *               (normally L_b - q_len, L_b the global length including the
+ *               q_len new tokens)
+ *   q           [batch, q_len, num_q_heads, qk_dim]
+ *   o_partial   [batch, q_len, num_q_heads, v_dim] fp32 (out)
+ *   lse_partial [batch, q_len, num_q_heads] fp32 (out); a query that sees no
+ *               token of this shard gets O = 0, LSE = -inf
+ * Other arguments as in dcp_decode_partial. With q_len 1 the result is that
+ * of dcp_decode_partial restricted to positions <= q_pos[b]. */
+dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t shard,
+                                    const int32_t* q_pos, const void* q, const void* k_cache,
+                                    const void* v_cache, const float* kv_scale,
+                                    const int32_t* local_block_table,
+                                    const int32_t* local_seq_lens, float* o_partial,
+                                    float* lse_partial, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /* LSE merge of num_partials partial results (summary section of the DCP blog
  * page, merge equation; the reweighting inside cp_lse_ag_out_rs of section A2):
@@ -230,8 +267,11 @@ dcp_status_t dcp_lse_merge(const float* o_partials, const float* lse_partials,
  * unsharded result (the whole AllGather-Q / Compute / AllGather+ReduceScatter
  * round of section A2, with the collectives replaced by on-device data).
  *   block_table [batch, max_blocks_per_seq] int32 (global), seq_lens [batch] int32
- *   out         [batch, num_q_heads, v_dim] of desc->out_dtype
- *   lse_out     [batch, num_q_heads] fp32 or NULL
+ *   out         [batch, q_len, num_q_heads, v_dim] of desc->out_dtype
+ *   lse_out     [batch, q_len, num_q_heads] fp32 or NULL
+ * With desc->q_len > 1 the queries are the last q_len positions of each
+ * sequence (query t at seq_len - q_len + t) and each sees the positions up to
+ * its own.
  * Other arguments as in dcp_decode_partial. */
 dcp_status_t dcp_decode_all_shards(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
                                    const void* v_cache, const float* kv_scale,

@@ -28,7 +28,8 @@ def desc_for(w, dev, out_dtype=dcp.F32, num_shards=None):
     return dcp.make_desc(kind, dev.q, dev.k_cache, dev.block_table,
                          num_shards=w.spec.num_shards if num_shards is None else num_shards,
                          v_dim=w.spec.v_dim, softmax_scale=w.spec.softmax_scale,
-                         max_seq_len=int(max(1, w.seq_lens.max(initial=0))), out_dtype=out_dtype)
+                         max_seq_len=int(max(1, w.seq_lens.max(initial=0))), out_dtype=out_dtype,
+                         q_len=getattr(w.spec, "q_len", 1))
 
 
 def to_np(t):

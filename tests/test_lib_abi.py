@@ -168,6 +168,22 @@ def test_remap_and_merge_argument_errors():
         dcp.DCP_ERR_INVALID_ARG
 
 
+def test_descriptor_without_q_len_reads_as_single_token():
+    d = mla_desc()
+    full = dcp.lib().dcp_workspace_size(ctypes.byref(d))
+    assert full > 0
+    d.struct_size = dcp.AttnDesc.q_len.offset  # a caller built before the q_len field
+    d.q_len = 7  # past the caller's struct: never read
+    assert dcp.lib().dcp_workspace_size(ctypes.byref(d)) == full
+    d.struct_size = dcp.AttnDesc.q_len.offset - 8
+    assert dcp.lib().dcp_workspace_size(ctypes.byref(d)) == 0
+    d = mla_desc()
+    d.q_len = 4  # 4 x 64 query rows per sequence: four times the partial rows
+    assert dcp.lib().dcp_workspace_size(ctypes.byref(d)) > full
+    d.q_len = 5  # 320 rows: more than the latent kernels take
+    assert dcp.lib().dcp_workspace_size(ctypes.byref(d)) == 0
+
+
 def test_status_strings_and_version():
     assert dcp.status_str(0) == "ok"
     assert "workspace" in dcp.status_str(3)

@@ -11,6 +11,10 @@ One step = one dcp_decode_all_shards call over the whole batch: work plan,
 attention over all D shards, and the LSE merge -- one decode token per
 sequence through one attention layer, inputs already resident in HBM.
 
+`--q-len N` times multi-token (draft) decode instead: N query tokens per
+sequence, each seeing the positions up to its own; `value` still counts each
+cached byte once per step and tok/s counts every query token.
+
 Prints one JSON line. `value` is KV GB/s: bytes of cached latent rows the step
 must read (sum of lengths x 1152 B) divided by the wall time of a step.
 `roofline.achieved` divides the same bytes by the attention kernel's own
@@ -204,6 +208,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true",
                     help="skip the per-call timings of remap, one shard's partial and the merge")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per sequence (multi-token decode when > 1)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (counter scaling)")
     args = ap.parse_args()
@@ -224,6 +230,10 @@ def main():
         sys.exit(1)
     dcp.lib()
     spec = W.SPECS[args.workload]
+    if args.q_len > 1:
+        from dataclasses import replace
+
+        spec = replace(spec, name=f"{spec.name}_q{args.q_len}", q_len=args.q_len)
     log(f"generating {spec.name} inputs on the host")
     t0 = time.perf_counter()
     w = W.make(spec)
@@ -233,11 +243,11 @@ def main():
     kind = dcp.KV_LATENT if spec.kind == "mla" else dcp.KV_SEPARATE
     desc = dcp.make_desc(kind, dev.q, dev.k_cache, dev.block_table, num_shards=spec.num_shards,
                          v_dim=spec.v_dim, softmax_scale=spec.softmax_scale,
-                         max_seq_len=int(w.seq_lens.max()))
+                         max_seq_len=int(w.seq_lens.max()), q_len=spec.q_len)
     ws = dcp.alloc_workspace(desc, "cuda")
-    out = torch.empty((spec.batch, spec.num_q_heads, spec.v_dim), dtype=torch.float32,
-                      device="cuda")
-    lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
+    rows = spec.q_len * spec.num_q_heads
+    out = torch.empty((spec.batch, rows, spec.v_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((spec.batch, rows), dtype=torch.float32, device="cuda")
 
     def step(events=None):
         dcp.decode_all_shards(desc, dev.q, dev.k_cache, dev.v_cache, dev.kv_scale,
@@ -277,7 +287,7 @@ def main():
         "dtype": spec.kv_dtype,
         "data": "synthetic",
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "tok_per_s_per_layer": round(spec.batch / (ms_per_step * 1e-3), 1),
+        "tok_per_s_per_layer": round(spec.batch * spec.q_len / (ms_per_step * 1e-3), 1),
         "config": {
             "workload": spec.name,
             "batch": spec.batch,
@@ -287,6 +297,7 @@ def main():
             "v_dim": spec.v_dim,
             "block_size": spec.block_size,
             "num_shards": spec.num_shards,
+            "q_len": spec.q_len,
             "sum_seq_len": int(w.seq_lens.sum()),
             "max_seq_len": int(w.seq_lens.max()),
             "kv_bytes": kv_bytes,
@@ -301,7 +312,7 @@ def main():
             "kernel_ms": round(attn_ms, 4),
         },
     }
-    if not args.no_components:
+    if not args.no_components and spec.q_len == 1:
         log("timing the path's calls one by one")
         result["components"] = components(dcp, desc, dev, w, ws)
     if not args.no_cpu_baseline:

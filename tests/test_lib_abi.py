@@ -104,6 +104,8 @@ INVALID = [
     ("misaligned token stride", lambda: mla_desc(kv_token_stride=577)),
     ("nan scale", lambda: mla_desc(softmax_scale=float("nan"))),
     ("bad dtype", lambda: mla_desc(kv_dtype=7)),
+    ("negative q_len", lambda: mla_desc(q_len=-1)),
+    ("q_len above 64", lambda: gqa_desc(q_len=65)),
 ]
 UNSUPPORTED = [
     ("latent width", lambda: mla_desc(qk_dim=512, v_dim=512, kv_token_stride=512,
@@ -116,6 +118,8 @@ UNSUPPORTED = [
     ("fp8 gqa", lambda: gqa_desc(q_dtype=dcp.BF16, kv_dtype=dcp.FP8_E4M3,
                                   kv_token_stride=8 * 128, kv_block_stride=16 * 8 * 128)),
     ("fp8 output", lambda: mla_desc(out_dtype=dcp.FP8_E4M3)),
+    ("latent 5 x 64 query rows", lambda: mla_desc(q_len=5)),
+    ("latent 2 x 8 heads", lambda: mla_desc(num_q_heads=8, q_len=2)),
 ]
 
 
@@ -182,6 +186,50 @@ def test_descriptor_without_q_len_reads_as_single_token():
     assert dcp.lib().dcp_workspace_size(ctypes.byref(d)) > full
     d.q_len = 5  # 320 rows: more than the latent kernels take
     assert dcp.lib().dcp_workspace_size(ctypes.byref(d)) == 0
+
+
+def test_append_update_and_mtp_argument_errors():
+    """Argument errors of the per-step entry points return before any HIP call."""
+    L = dcp.lib()
+    d = mla_desc()
+
+    def append(desc=d, n=1, shard=-1, new_dtype=dcp.BF16, k_new=FAKE, pos=FAKE, table=FAKE,
+               k=FAKE, scale=FAKE):
+        return L.dcp_kv_append(ctypes.byref(desc), n, None, pos, k_new, None, new_dtype, shard,
+                               table, k, None, scale, None)
+
+    assert append(n=-1) == dcp.DCP_ERR_INVALID_ARG
+    assert append(shard=8) == dcp.DCP_ERR_INVALID_ARG
+    assert append(shard=-2) == dcp.DCP_ERR_INVALID_ARG
+    assert append(new_dtype=dcp.F32) == dcp.DCP_ERR_UNSUPPORTED  # bf16 cache takes bf16 rows
+    assert append(new_dtype=9) == dcp.DCP_ERR_INVALID_ARG
+    assert append(pos=None) == dcp.DCP_ERR_INVALID_ARG
+    assert append(k_new=ctypes.c_void_p((1 << 20) + 8)) == dcp.DCP_ERR_INVALID_ARG
+    assert append(desc=mla_desc(num_q_heads=0)) == dcp.DCP_ERR_INVALID_ARG
+    f8 = mla_desc(kv_dtype=dcp.FP8_E4M3)
+    assert append(desc=f8, scale=None) == dcp.DCP_ERR_INVALID_ARG
+    assert append(desc=f8, new_dtype=dcp.FP8_E4M3) == dcp.DCP_ERR_UNSUPPORTED
+    assert append(n=0, pos=None) == dcp.DCP_OK  # nothing to write, nothing enqueued
+    g = gqa_desc()
+    assert L.dcp_kv_append(ctypes.byref(g), 1, None, FAKE, FAKE, None, dcp.BF16, -1, FAKE, FAKE,
+                           FAKE, None, None) == dcp.DCP_ERR_INVALID_ARG  # GQA needs v rows
+    assert L.dcp_block_remap_update(FAKE, None, FAKE, 1, 1, 1, 1, FAKE, FAKE, None) == \
+        dcp.DCP_ERR_INVALID_ARG
+    assert L.dcp_block_remap_update(FAKE, FAKE, FAKE, 0, 1, 1, 1, FAKE, FAKE, None) == \
+        dcp.DCP_ERR_INVALID_ARG
+    assert L.dcp_block_remap_update(FAKE, FAKE, FAKE, 1, 1, 1, 0, FAKE, FAKE, None) == \
+        dcp.DCP_ERR_INVALID_ARG
+
+    def mtp(desc, shard=0, qpos=FAKE):
+        return L.dcp_decode_partial_mtp(ctypes.byref(desc), shard, qpos, FAKE, FAKE, None, None,
+                                        FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+
+    m2 = mla_desc(q_len=2)
+    assert mtp(m2, shard=8) == dcp.DCP_ERR_INVALID_ARG
+    assert mtp(m2, shard=-1) == dcp.DCP_ERR_INVALID_ARG
+    assert mtp(m2, qpos=None) == dcp.DCP_ERR_INVALID_ARG
+    assert L.dcp_decode_partial(ctypes.byref(m2), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, 1 << 40, None) == dcp.DCP_ERR_INVALID_ARG
 
 
 def test_status_strings_and_version():

@@ -903,7 +903,10 @@ __device__ __forceinline__ i32x4 f8x8_to_f16x8(int d0, int d1) {
                __builtin_bit_cast(int, h3)};
 }
 
-template <bool FP8>
+// SHARED: several head groups (more than 64 query rows per sequence) stream
+// the same tiles. Their work groups run side by side on one XCD and the copies
+// keep the default cache policy, so the second group finds the tiles in L2.
+template <bool FP8, bool SHARED>
 __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   using E = Elt<FP8>;
   using P = PP<FP8>;
@@ -922,8 +925,12 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   const int grp = w & 3;  // score waves: head group; value waves: value slice
   const int q4 = lane >> 4;
   const int l16 = lane & 15;
-  const int g = xcd_logical_group(blockIdx.x, kGroups);
-  const int head0 = blockIdx.y * 64;
+  // Head groups of one range are consecutive on one XCD (hardware dispatches
+  // work group i to XCD i % 8): group i covers range g and head group y.
+  const int ngrp = gridDim.x / kGroups;
+  const int k8 = blockIdx.x >> 3;
+  const int g = (blockIdx.x & 7) * (kGroups >> 3) + k8 / ngrp;
+  const int head0 = (k8 % ngrp) * 64;
   const int total = a.hdr->total;
   const int range0 = a.wg_start[g];
   const int end = a.wg_start[g + 1];
@@ -1065,7 +1072,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         if (code && cp_row[n] < sr.nvalid) src = sr.base + cp_off[n];
         if (scl && lane < 8 && 4 * lane < sr.nvalid) src = sr.sbase + 16 * lane;
         DCP_LDS char* ldst = code ? stage + ii * 1024 : scl ? stage + P::kScaleOff : ring + P::kPadOff;
-        __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, kCopyPolicy);
+        __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, SHARED ? 0 : kCopyPolicy);
         return;
       }
     } else {
@@ -1075,7 +1082,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
     // builtin's argument list the host pass drops this kernel's stub.)
     const char* src = cp_row[n] < sr.nvalid ? sr.base + cp_off[n] : a.zero;
     DCP_LDS char* ldst = stage + ii * 1024;
-    __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, kCopyPolicy);
+    __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, SHARED ? 0 : kCopyPolicy);
   };
 
   // The two roles run the same loops and barriers with separate code, so the
@@ -1807,8 +1814,15 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   const int heads = a.Hq < 64 ? a.Hq : 64;
   const dim3 grid(kGroups, a.Hq / heads);
   if (use_pp(d)) {
-    if (fp8) hipLaunchKernelGGL(mla_pp_kernel<true>, grid, dim3(512), 0, stream, a);
-    else hipLaunchKernelGGL(mla_pp_kernel<false>, grid, dim3(512), 0, stream, a);
+    const int ngrp = a.Hq / 64;
+    const dim3 pgrid(kGroups * ngrp);
+    if (ngrp > 1) {
+      if (fp8) hipLaunchKernelGGL((mla_pp_kernel<true, true>), pgrid, dim3(512), 0, stream, a);
+      else hipLaunchKernelGGL((mla_pp_kernel<false, true>), pgrid, dim3(512), 0, stream, a);
+    } else {
+      if (fp8) hipLaunchKernelGGL((mla_pp_kernel<true, false>), pgrid, dim3(512), 0, stream, a);
+      else hipLaunchKernelGGL((mla_pp_kernel<false, false>), pgrid, dim3(512), 0, stream, a);
+    }
     return hipGetLastError();
   }
   switch (heads / 16) {

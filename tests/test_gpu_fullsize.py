@@ -47,19 +47,26 @@ def _sample(lens):
     return sorted(set(picks))
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_rows(name):
-    spec = W.SPECS[name]
+# (workload, query tokens per sequence): single-token decode at every size,
+# and multi-token decode as `bench.py --q-len 2` times it.
+CASES = [(n, 1) for n in FULL] + [("mla_bf16_b64_bimodal", 2), ("gqa_bf16_b32_L32k", 2)]
+
+
+@pytest.mark.parametrize("name,q_len", CASES, ids=[f"{n}-q{q}" for n, q in CASES])
+def test_full_size_sampled_rows(name, q_len):
+    from dataclasses import replace
+
+    spec = replace(W.SPECS[name], q_len=q_len)
     w = W.make(spec)
     dev = W.to_torch(w, "cuda")
     kind = dcp.KV_LATENT if spec.kind == "mla" else dcp.KV_SEPARATE
     desc = dcp.make_desc(kind, dev.q, dev.k_cache, dev.block_table, num_shards=spec.num_shards,
                          v_dim=spec.v_dim, softmax_scale=spec.softmax_scale,
-                         max_seq_len=int(w.seq_lens.max()))
+                         max_seq_len=int(w.seq_lens.max()), q_len=q_len)
     ws = dcp.alloc_workspace(desc, "cuda")
-    out = torch.empty((spec.batch, spec.num_q_heads, spec.v_dim), dtype=torch.float32,
-                      device="cuda")
-    lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
+    rows_per_seq = q_len * spec.num_q_heads
+    out = torch.empty((spec.batch, rows_per_seq, spec.v_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((spec.batch, rows_per_seq), dtype=torch.float32, device="cuda")
     for _ in range(2):  # the second call reuses the workspace as the benchmark does
         dcp.decode_all_shards(desc, dev.q, dev.k_cache, dev.v_cache, dev.kv_scale,
                               dev.block_table, dev.seq_lens, workspace=ws, out=out, lse_out=lse)

@@ -169,12 +169,27 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
         const int g1 = min(G - 1, static_cast<int>(y1 / cc));
         lo = b + g0;
         hi = b + g1 + 1;
-        for (int gg = g0 + 1; gg < g1; ++gg)
-          if (wo[gg] == wo[gg + 1])
-            for (int h = 0; h < Hq; ++h) lse[static_cast<size_t>(b + gg) * Hq + h] = -INFINITY;
       }
       seq_slots[2 * b] = lo;
       seq_slots[2 * b + 1] = hi;
+    }
+    // The gaps, one thread per work group: a work group without blocks lies
+    // strictly inside sequence b's range exactly when the blocks just before
+    // and just after it (x - 1 and x) both belong to b.
+    auto seq_of = [&](int blk) {  // last sequence starting at or before block blk
+      int lo = 0, hi = m.batch;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (so[mid * m.D] <= blk) lo = mid; else hi = mid;
+      }
+      return lo;
+    };
+    for (int g = t + 1; g < G; g += 1024) {
+      const int x = wo[g];
+      if (x != wo[g + 1] || x <= 0 || x >= total) continue;
+      const int b = seq_of(x - 1);
+      if (b == seq_of(x))
+        for (int h = 0; h < Hq; ++h) lse[static_cast<size_t>(b + g) * Hq + h] = -INFINITY;
     }
     return;
   }

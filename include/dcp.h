@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
   DCP_OK = 0,
   DCP_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad stride or alignment */
-  DCP_ERR_UNSUPPORTED = 2, /* a valid combination this build has no kernel for */
+  DCP_ERR_UNSUPPORTED = 2, /* a valid combination the library has no kernel for */
   DCP_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dcp_workspace_size() */
   DCP_ERR_HIP = 4          /* the HIP runtime rejected a launch */
 } dcp_status_t;
@@ -103,7 +103,7 @@ typedef struct {
 /* Smallest struct_size accepted: descriptors from before the q_len field. */
 #define DCP_ATTN_DESC_MIN_SIZE offsetof(dcp_attn_desc_t, q_len)
 
-/* Supported kernels in this build:
+/* Shapes and types the library has kernels for:
  *   DCP_KV_SEPARATE: q_dtype == kv_dtype in {F32, BF16}; qk_dim == v_dim in
  *     {64, 128}; num_q_heads % num_kv_heads == 0.
  *   DCP_KV_LATENT: q BF16; kv BF16, or FP8_E4M3 with kv_scale; qk_dim 576,

@@ -350,46 +350,46 @@ hipError_t launch_merge_partials(const float* o, const float* lse, int P, int B,
 }
 
 // ------------------------------------------------------------------ remap
-// One thread per local-table entry [r, b, i]; entries with i == 0 also write
-// the shard's token count for sequence b. Interleaved ownership: entry i of
-// shard r is logical block r + D*i. Contiguous ownership (the 200K-token
-// four-way split of the DCP blog page, section A2): a sequence of nb blocks is
-// cut into runs of c = ceil(nb / D) blocks and entry i of shard r is logical
-// block r*c + i.
+// One work group per (shard r, sequence b) row of the local table; its
+// threads walk the row's entries i, and thread 0 writes the shard's token
+// count for sequence b. Interleaved ownership: entry i of shard r is logical
+// block r + D*i. Contiguous ownership (the 200K-token four-way split of the
+// DCP blog page, section A2): a sequence of nb blocks is cut into runs of
+// c = ceil(nb / D) blocks and entry i of shard r is logical block r*c + i.
 __global__ __launch_bounds__(256) void remap_kernel(const int32_t* __restrict__ table,
                                                     const int32_t* __restrict__ lens, int B,
                                                     int max_blocks, int bs, int D, int width,
                                                     int contiguous,
                                                     int32_t* __restrict__ local_table,
                                                     int32_t* __restrict__ local_lens) {
-  const long long total = static_cast<long long>(D) * B * width;
-  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int i = static_cast<int>(idx % width);
-  const int b = static_cast<int>((idx / width) % B);
-  const int r = static_cast<int>(idx / (static_cast<long long>(width) * B));
+  const int r = blockIdx.x / B;
+  const int b = blockIdx.x - r * B;
   long long L = lens[b];
   const long long cap = static_cast<long long>(max_blocks) * bs;
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int nb = static_cast<int>((L + bs - 1) / bs);
+  const int32_t* trow = table + static_cast<size_t>(b) * max_blocks;
+  int32_t* lrow = local_table + static_cast<size_t>(blockIdx.x) * width;
   if (contiguous) {
     const int c = (nb + D - 1) / D;  // c <= width because nb <= max_blocks
-    const int j = r * c + i;
-    local_table[idx] = (i < c && j < nb) ? table[static_cast<size_t>(b) * max_blocks + j] : -1;
-    if (i == 0) {
-      const long long lo = static_cast<long long>(r) * c * bs;
-      const long long hi = lo + static_cast<long long>(c) * bs;
-      const long long n = (hi < L ? hi : L) - lo;
-      local_lens[static_cast<size_t>(r) * B + b] = static_cast<int32_t>(n > 0 ? n : 0);
+    const int j0 = r * c;
+    for (int i = threadIdx.x; i < width; i += blockDim.x)
+      lrow[i] = (i < c && j0 + i < nb) ? trow[j0 + i] : -1;
+    if (threadIdx.x == 0) {
+      const long long lo = static_cast<long long>(j0) * bs;
+      const long long n = (lo + static_cast<long long>(c) * bs < L ? lo + static_cast<long long>(c) * bs : L) - lo;
+      local_lens[blockIdx.x] = static_cast<int32_t>(n > 0 ? n : 0);
     }
     return;
   }
-  const int j = r + D * i;
-  local_table[idx] = j < nb ? table[static_cast<size_t>(b) * max_blocks + j] : -1;
-  if (i == 0) {
+  for (int i = threadIdx.x; i < width; i += blockDim.x) {
+    const int j = r + D * i;
+    lrow[i] = j < nb ? trow[j] : -1;
+  }
+  if (threadIdx.x == 0) {
     const int n_r = nb > r ? (nb - r + D - 1) / D : 0;
     const int tail = (nb > 0 && (nb - 1) % D == r) ? static_cast<int>(static_cast<long long>(nb) * bs - L) : 0;
-    local_lens[static_cast<size_t>(r) * B + b] = n_r * bs - tail;
+    local_lens[blockIdx.x] = n_r * bs - tail;
   }
 }
 
@@ -397,10 +397,8 @@ hipError_t launch_remap(const int32_t* table, const int32_t* lens, int B, int ma
                         int D, bool contiguous, int32_t* local_table, int32_t* local_lens,
                         hipStream_t stream) {
   const int width = (max_blocks + D - 1) / D;
-  const long long total = static_cast<long long>(D) * B * width;
-  const int threads = 256;
-  const long long blocks = (total + threads - 1) / threads;
-  hipLaunchKernelGGL(remap_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream,
+  const int threads = width >= 256 ? 256 : (width >= 128 ? 128 : 64);
+  hipLaunchKernelGGL(remap_kernel, dim3(static_cast<unsigned>(D) * B), dim3(threads), 0, stream,
                      table, lens, B, max_blocks, bs, D, width, contiguous ? 1 : 0, local_table,
                      local_lens);
   return hipGetLastError();

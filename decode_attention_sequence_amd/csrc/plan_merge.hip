@@ -49,11 +49,34 @@ WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim) 
 // seg_cost blocks' worth of fixed work (starting a piece, storing its
 // partial), so a work group whose range crosses many short segments gets
 // fewer blocks. Work group g takes the blocks whose cost positions fall in
-// [g cc, (g + 1) cc), cc = ceil(total cost / G); a segment's overhead units
-// come before its first block.
+// [start(g), start(g + 1)); a segment's overhead units come before its first
+// block.
+// Range g runs on XCD g / (G / 8) (xcd_logical_group). On MI355X the
+// odd-numbered XCDs finish the same work 2-4 % later than the even ones
+// (per-work-group finishing times on three boxes, whatever ranges they get),
+// so their ranges get a share of the cost smaller by kWOdd / kWEven.
 // Arrays the plan searches are mirrored in LDS when they fit (flat pointers
 // then address LDS), else read from the workspace.
 constexpr int kPlanLds = 6144;  // entries per mirrored array
+constexpr int kWEven = 40, kWOdd = 39;
+
+// First cost position of range g (start(G) = total cost). Below 8 cost units
+// per range the split is uniform, cc = ceil(total / G) units per range, which
+// leaves no range without cost units before the last block; above it the
+// weighted ranges all hold several units as well.
+__device__ __forceinline__ int split_start(int total_c, int G, int g) {
+  if ((G & 7) || total_c < 8 * G) {
+    const long long cc = max(1, (total_c + G - 1) / G);
+    return static_cast<int>(min(static_cast<long long>(g) * cc, static_cast<long long>(total_c)));
+  }
+  const int per = G >> 3;
+  const int x = g / per, k = g - x * per;
+  const long long w = static_cast<long long>((x + 1) >> 1) * per * kWEven +
+                      static_cast<long long>(x >> 1) * per * kWOdd +
+                      static_cast<long long>(k) * ((x & 1) ? kWOdd : kWEven);
+  const long long all = 4ll * per * (kWEven + kWOdd);
+  return static_cast<int>(static_cast<long long>(total_c) * w / all);
+}
 
 __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int seg_cost, int Hq,
                                                     int seq_pieces, PlanHeader* hdr, int32_t* seg_off,
@@ -64,6 +87,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
   __shared__ int l_seg[kPlanLds];
   __shared__ int l_cost[kPlanLds];
   __shared__ int l_wg[kPlanLds];
+  __shared__ int l_sc[kPlanLds];  // split_start of each range
   const bool mirror_s = S + 1 <= kPlanLds;
   const bool mirror_g = G + 1 <= kPlanLds;
   const int t = threadIdx.x;
@@ -128,9 +152,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
   const int* co = mirror_s ? l_cost : cost_off;
   // (Costs stay below 2^31: they count blocks of int32 table entries plus a
   // few units per segment, so 32-bit arithmetic suffices.)
-  const unsigned cc = static_cast<unsigned>(max(1, (total_c + G - 1) / G));
   for (int g = t; g <= G; g += 1024) {
-    const long long y = min(static_cast<long long>(g) * cc, static_cast<long long>(total_c));
+    const int y = split_start(total_c, G, g);
+    if (mirror_g) l_sc[g] = y;
     // last segment s < S with cost_off[s] <= y
     int lo = 0, hi = S;
     while (hi - lo > 1) {
@@ -145,14 +169,24 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
     wg_start[g] = g == 0 ? 0 : x;
     if (mirror_g) l_wg[g] = g == 0 ? 0 : x;
   }
-  // The work group of block i of segment s is floor(cost position / cc), the
-  // cost position being cost_off[s] + seg_cost + i (the same split as above).
+  // The work group of block i of segment s is the range holding its cost
+  // position cost_off[s] + seg_cost + i (the same split as above): the last g
+  // with start(g) <= that position.
+  __syncthreads();  // wg_start and the split starts complete
+  auto range_of = [&](unsigned y) {
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      const int st = mirror_g ? l_sc[mid] : split_start(total_c, G, mid);
+      if (static_cast<unsigned>(st) <= y) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
   if (seq_pieces) {
     // One partial per work group and sequence: sequence b's blocks (contiguous
     // over its segments) lie in work groups g0..g1, whose partials sit in slots
     // b + g0 .. b + g1. A work group in between without blocks leaves its slot
     // unwritten: it gets LSE = -inf (an empty partial).
-    __syncthreads();  // wg_start complete
     const int* wo = mirror_g ? l_wg : wg_start;
     for (int b = t; b < m.batch; b += 1024) {
       int s_first = -1, s_last = -1;
@@ -165,8 +199,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
       if (s_first >= 0) {
         const unsigned y0 = static_cast<unsigned>(co[s_first] + seg_cost);
         const unsigned y1 = static_cast<unsigned>(co[s_last] + seg_cost + (so[s_last + 1] - so[s_last]) - 1);
-        const int g0 = min(G - 1, static_cast<int>(y0 / cc));
-        const int g1 = min(G - 1, static_cast<int>(y1 / cc));
+        const int g0 = range_of(y0);
+        const int g1 = range_of(y1);
         lo = b + g0;
         hi = b + g1 + 1;
       }
@@ -204,8 +238,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
       const int nb = so[s + 1] - so[s];
       if (nb <= 0) continue;
       const unsigned y0 = static_cast<unsigned>(co[s] + seg_cost);
-      const int s_lo = s + min(G - 1, static_cast<int>(y0 / cc));
-      const int s_hi = s + min(G - 1, static_cast<int>((y0 + nb - 1) / cc)) + 1;
+      const int s_lo = s + range_of(y0);
+      const int s_hi = s + range_of(y0 + nb - 1) + 1;
       if (hi == 0) lo = s_lo;
       else
         for (int x = hi; x < s_lo; ++x)

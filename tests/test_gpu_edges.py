@@ -2,11 +2,12 @@
 shard counts above the block count, other head counts, and unusable block ids."""
 import numpy as np
 import pytest
+import torch
 
 import decode_attention_sequence_amd as dcp
 import oracle
 import workloads as W
-from gpu_helpers import TOL, compare, need_gpu, run_all_shards, run_per_shard
+from gpu_helpers import TOL, compare, desc_for, need_gpu, run_all_shards, run_per_shard
 
 pytestmark = pytest.mark.gpu
 
@@ -98,3 +99,40 @@ def test_sharp_softmax(kind, dtype, bs, hq, hkv, dim):
     o_ref, lse_ref = oracle.decode_reference(w)
     o, lse, _, _ = run_all_shards(w)
     compare(o, lse, o_ref, lse_ref, **TOL[dtype], label="sharp softmax")
+
+
+@pytest.mark.parametrize("kind,dtype", [("mla", "bf16"), ("mla", "fp8"), ("gqa", "bf16")])
+def test_device_lengths_are_clamped(kind, dtype):
+    """Device-resident lengths are not validated: a negative length reads as 0 and a
+    length past the table's reach reads as the table width times the block size."""
+    dim = 576 if kind == "mla" else 128
+    bs = 64 if kind == "mla" else 16
+    hq, hkv = (64, 1) if kind == "mla" else (16, 2)
+    lens = [3 * bs + 5, 2 * bs, 1]
+    w = _workload(kind, dtype, bs, 4, hq, hkv, dim, lens)
+    dev = W.to_torch(w)
+    desc = desc_for(w, dev)
+    mb = w.block_table.shape[1]
+    o_ref, lse_ref = oracle.decode_reference(w)
+    bad = torch.tensor([-5, 10 ** 6, 1], dtype=torch.int32, device="cuda")
+    o, lse = dcp.decode_all_shards(desc, dev.q, dev.k_cache, dev.v_cache, dev.kv_scale,
+                                   dev.block_table, bad)
+    torch.cuda.synchronize()
+    # Sequence 0 reads as empty. Sequence 1 reads as mb * bs tokens, but its row
+    # maps only its own blocks (the rest are -1, skipped): the result is its
+    # attention over those, the same as for its true length.
+    assert mb * bs > 2 * bs
+    o_ref[0], lse_ref[0] = 0.0, -np.inf
+    compare(o, lse, o_ref, lse_ref, **TOL[dtype], label="clamped lengths")
+
+
+def test_empty_cache_pool():
+    """num_cache_blocks = 0 with null cache pointers: every sequence is empty."""
+    w = _workload("mla", "bf16", 64, 8, 64, 1, 576, [100, 7])
+    dev = W.to_torch(w)
+    empty = torch.empty((0, 64, 576), dtype=torch.bfloat16, device="cuda")
+    desc = dcp.make_desc(dcp.KV_LATENT, dev.q, empty, dev.block_table, num_shards=8, v_dim=512,
+                         max_seq_len=100)
+    o, lse = dcp.decode_all_shards(desc, dev.q, None, None, None, dev.block_table, dev.seq_lens)
+    torch.cuda.synchronize()
+    assert float(o.abs().max()) == 0.0 and bool((lse == -np.inf).all())

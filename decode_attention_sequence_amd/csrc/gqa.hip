@@ -5,19 +5,22 @@
 // query heads; under DCP each shard attends the full query against its own
 // blocks of the shared head and returns a partial output with its LSE.
 //
-// Work: the same stream-K ranges as the latent kernel, times the KV heads
-// (grid = ranges x Hkv). Cache layout [block, token, kv_head, dim].
+// Work: the same stream-K ranges as the latent kernel, times the KV heads and
+// their column tiles (grid = ranges x (Hkv x column tiles)). The query rows of
+// one KV head are its group's heads for every query token (several tokens in
+// multi-token decode), taken 16 at a time. Cache layout
+// [block, token, kv_head, dim].
 //
-// bf16 kernel: one wave per (range, KV head). 32-token K and V tiles are
-// copied HBM -> LDS with 16-byte direct-to-LDS loads (two stages); the
-// query group (up to 16 heads) forms the N = 16 side of
-// v_mfma_f32_16x16x32_bf16: S^T = K_tile . Q^T, then O^T += V_tile^T . P^T
-// with the transposed V operand read by ds_read_b64_tr_b16. The group is
-// padded to 16 columns with zero queries; padded columns are never stored.
+// bf16 kernel: one wave per (range, KV head, column tile). 32-token K and V
+// tiles are copied HBM -> LDS with 16-byte direct-to-LDS loads (two stages);
+// the tile's query rows form the N = 16 side of v_mfma_f32_16x16x32_bf16:
+// S^T = K_tile . Q^T, then O^T += V_tile^T . P^T with the transposed V operand
+// read by ds_read_b64_tr_b16. A tile with fewer than 16 rows is padded with
+// zero queries; padded columns are never stored.
 // At 8 flop per cache byte this path is bound by HBM, not by the MFMA pipe.
 //
 // fp32 kernel: plain VALU, one lane per token for the scores and one lane per
-// value column for the weighted sum.
+// value column for the weighted sum, over up to 16 query rows per wave.
 #include "dcp_internal.hpp"
 
 namespace dcp {
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(64) void gqa_bf16_kernel(GqaArgs a) {
   }
 }
 
-// fp32: one wave per (range, KV head). Scores: lane = token of a 64-token
+// fp32: one wave per (range, KV head, column tile). Scores: lane = token of a 64-token
 // tile; weighted sum: lane = value column (DH / 64 columns per lane).
 template <int DH>
 __global__ __launch_bounds__(64) void gqa_f32_kernel(GqaArgs a) {

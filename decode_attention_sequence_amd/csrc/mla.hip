@@ -804,6 +804,13 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
 //    lane reads its eight tokens of one column pair with ds_read_b64_tr_b8,
 //    one read per M tile. The token scale multiplies the fp32 score and the
 //    probability that weights the token's value (rounded to fp16).
+//  * More than 64 query rows per sequence (more heads, or several query
+//    tokens in multi-token decode, rows token-major): one work group per
+//    (range, 64-row head group), the head groups of a range dispatched next to
+//    each other on one XCD so that they read its tiles through the same L2.
+//    In multi-token decode a head group holds one query token, which sees the
+//    positions up to its own: its tile table clamps each tile's row count at
+//    that position.
 template <bool FP8>
 struct PP {
   static constexpr int kRowBytes = FP8 ? kF8RowB : kRowB;    // cache row bytes in LDS

@@ -10,7 +10,8 @@ It computes, in float64 with NumPy, exactly what the pages define:
   global-to-local block-table remap -- "vLLM长序列推理优化：DCP切分KV Cache原理与实战",
   sections 2.2 and 3.2; contiguous ownership (each shard one consecutive
   chunk of a sequence) -- "Efficient Decode Context Parallelism with vLLM for
-  Long Context Workloads", section A2;
+  Long Context Workloads", section A2; token-level interleave (the token at
+  position t on shard t mod D) -- "vLLM长序列推理优化", sections 2.2 and 3.4;
 * single-token softmax attention over a paged cache, unsharded, with GQA
   head sharing and absorbed-MLA latent rows -- "Efficient Decode Context
   Parallelism with vLLM for Long Context Workloads", section A2 (Compute step);
@@ -39,8 +40,11 @@ from .paged import (
     local_lengths,
     owner_of_block,
     local_index_of_block,
+    owner_of_token,
+    local_index_of_token,
     remap_block_table,
     shard_blocks,
+    token_local_lengths,
     tokens_in_block,
 )
 from .attention import (
@@ -71,8 +75,11 @@ __all__ = [
     "local_lengths",
     "owner_of_block",
     "local_index_of_block",
+    "owner_of_token",
+    "local_index_of_token",
     "remap_block_table",
     "shard_blocks",
+    "token_local_lengths",
     "tokens_in_block",
     "attend",
     "decode_reference",

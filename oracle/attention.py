@@ -36,7 +36,7 @@ qk_dim latent columns and the value is the first v_dim columns.
 import numpy as np
 
 from .codecs import bf16_to_f64, e4m3_to_f64
-from .paged import gather_rows, owner_of_block, blocks_of, tokens_in_block
+from .paged import gather_rows, owner_of_block, owner_of_token, blocks_of, tokens_in_block
 
 
 def attend(q, k, v, scale):
@@ -137,7 +137,11 @@ def decode_reference(w, batch_indices=None):
 
 
 def shard_positions(seq_len, block_size, num_shards, shard, ownership="interleaved"):
-    """Token positions held by ``shard``: the tokens of its owned blocks."""
+    """Token positions held by ``shard``: the tokens of its owned blocks (or,
+    under token-level interleave, the tokens it owns one by one)."""
+    if ownership == "token":
+        return np.asarray([t for t in range(int(seq_len)) if owner_of_token(t, num_shards) == shard],
+                          dtype=np.int64)
     pos = []
     nb = blocks_of(seq_len, block_size)
     for j in range(nb):

@@ -19,11 +19,17 @@ holding tokens 0-50K, GPU 1 50K-100K, and so on). At block granularity this
 reads: the nb blocks of a sequence form D consecutive chunks of
 c = ceil(nb / D) blocks, shard r owning blocks [r c, (r + 1) c) (the last
 chunks may be short or empty), with local index j - r c.
+
+Token-level interleave, the finer granularity section 2.2 of the practice
+page sets beside block-level splitting; its section 3.4 gives the example
+"rank 0 holds positions 0, 4, 8, ..., rank 1 holds 1, 5, 9, ..." at D = 4.
+Reading: the token at position t belongs to shard t mod D, at local index
+t // D, whatever the block size.
 """
 import numpy as np
 
 
-OWNERSHIPS = ("interleaved", "contiguous")
+OWNERSHIPS = ("interleaved", "contiguous", "token")
 
 
 def blocks_of(seq_len: int, block_size: int) -> int:
@@ -55,6 +61,16 @@ def local_index_of_block(j: int, num_shards: int, ownership: str = "interleaved"
     raise ValueError(ownership)
 
 
+def owner_of_token(t: int, num_shards: int) -> int:
+    """Token-level interleave: the token at position t lives on shard t mod D."""
+    return t % num_shards
+
+
+def local_index_of_token(t: int, num_shards: int) -> int:
+    """Token-level interleave: its index among that shard's tokens."""
+    return t // num_shards
+
+
 def tokens_in_block(j: int, seq_len: int, block_size: int) -> int:
     """Valid tokens in logical block j of a sequence of seq_len tokens."""
     return max(0, min(block_size, seq_len - j * block_size))
@@ -69,8 +85,13 @@ def shard_blocks(seq_len: int, block_size: int, num_shards: int, shard: int,
 
 def local_lengths(seq_len: int, block_size: int, num_shards: int,
                   ownership: str = "interleaved") -> list:
-    """Tokens each shard holds for one sequence, by counting its blocks."""
+    """Tokens each shard holds for one sequence, by counting its blocks (or,
+    under token-level interleave, its tokens)."""
     out = [0] * num_shards
+    if ownership == "token":
+        for t in range(int(seq_len)):
+            out[owner_of_token(t, num_shards)] += 1
+        return out
     nb = blocks_of(seq_len, block_size)
     for j in range(nb):
         out[owner_of_block(j, num_shards, ownership, nb)] += tokens_in_block(j, seq_len, block_size)
@@ -101,6 +122,17 @@ def remap_block_table(block_table, seq_lens, block_size: int, num_shards: int,
             local[r, b, i] = table[b, j]
             local_len[r, b] += tokens_in_block(j, int(lens[b]), block_size)
     return local, local_len
+
+
+def token_local_lengths(seq_lens, num_shards: int):
+    """Token-level interleave: int32 [D, B], the tokens shard r holds of
+    sequence b. Every block carries tokens of several shards, so the global
+    block table serves every shard and there is no local table."""
+    lens = np.asarray(seq_lens)
+    out = np.zeros((num_shards, len(lens)), dtype=np.int32)
+    for b, L in enumerate(lens):
+        out[:, b] = local_lengths(int(L), 1, num_shards, ownership="token")
+    return out
 
 
 def gather_rows(cache, table_row, positions, block_size: int):

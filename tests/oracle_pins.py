@@ -284,6 +284,47 @@ def check_contiguous_bruteforce(O):
                 assert llen[r, b] == tok, (d, b, r)
 
 
+def check_token_worked_example(O):
+    """Token-level interleave against the positions of the practice page's section 3.4."""
+    g = _golden("token_interleave.json")
+    d, bs, L = g["num_shards"], g["block_size"], g["seq_len"]
+    for r, want in g["positions"].items():
+        got = [int(x) for x in O.shard_positions(L, bs, d, int(r), ownership="token")]
+        assert got == want, (r, got)
+        for p in want:
+            assert O.owner_of_token(p, d) == int(r)
+    for e in g["local_index"]:
+        assert O.owner_of_token(e["position"], d) == e["shard"]
+        assert O.local_index_of_token(e["position"], d) == e["local"]
+    assert O.local_lengths(L, bs, d, ownership="token") == [len(v) for v in g["positions"].values()]
+
+
+def check_token_bruteforce(O):
+    """Token-level interleave: every position owned exactly once, local indices
+    counting the shard's tokens in order, and lengths summing to L."""
+    for bs in (1, 5, 16, 64):
+        for d in range(1, 10):
+            for L in list(range(0, 70)) + [97, 128, 255, 299]:
+                owned = []
+                lens = O.local_lengths(L, bs, d, ownership="token")
+                assert sum(lens) == L, (L, bs, d)
+                for r in range(d):
+                    pos = [int(x) for x in O.shard_positions(L, bs, d, r, ownership="token")]
+                    assert len(pos) == lens[r] == len(range(r, L, d)), (L, bs, d, r)
+                    for k, p in enumerate(pos):
+                        assert O.owner_of_token(p, d) == r
+                        assert O.local_index_of_token(p, d) == k
+                    assert pos == sorted(pos)
+                    owned.extend(pos)
+                assert sorted(owned) == list(range(L)), (L, bs, d)
+    lens = np.array([0, 1, 7, 8, 9, 100, 257])
+    for d in (1, 2, 3, 4, 8):
+        tl = O.token_local_lengths(lens, d)
+        assert tl.shape == (d, len(lens))
+        for b, L in enumerate(lens):
+            assert list(tl[:, b]) == [len(range(r, int(L), d)) for r in range(d)]
+
+
 # ----------------------------------------------------------------- attention
 def _brute(q, k, v, scale):
     """Pure-Python loops, math.exp/math.log only."""
@@ -422,6 +463,12 @@ def check_shard_merge_equals_unsharded(O):
             o, lse = O.lse_merge(op, lp)
             _close(o, o_ref, 1e-12, 1e-13)
             _close(lse, lse_ref, 1e-12, 1e-13)
+            # The merged result does not depend on which shard owns which token.
+            for own in ("contiguous", "token"):
+                op2, lp2 = O.shard_partials(w, d, ownership=own)
+                o2, lse2 = O.lse_merge(op2, lp2)
+                _close(o2, o_ref, 1e-12, 1e-13)
+                _close(lse2, lse_ref, 1e-12, 1e-13)
             m, l, ou = O.ml_partials(w, d)
             o2, lse2 = O.ml_merge(m, l, ou)
             _close(o2, o, 1e-12, 1e-13)
@@ -629,6 +676,8 @@ ALL_CHECKS = [
     check_ownership_bruteforce,
     check_contiguous_worked_example,
     check_contiguous_bruteforce,
+    check_token_worked_example,
+    check_token_bruteforce,
     check_attend_bruteforce,
     check_attend_sdpa,
     check_closed_forms,

@@ -54,6 +54,12 @@ MUTANTS = [
     ("paged.py", "return j // chunk_of(nb, num_shards)",
      "return min(num_shards - 1, j * num_shards // max(nb, 1))", "contiguous chunks balanced differently"),
     ("paged.py", "return j % num_shards", "return (j + 1) % num_shards", "owner off by one"),
+    ("paged.py", "return t % num_shards", "return (t + 1) % num_shards", "token owner off by one"),
+    ("paged.py", "return t // num_shards", "return t // num_shards + (t % num_shards > 0)",
+     "token local index rounded up"),
+    ("attention.py", "if owner_of_token(t, num_shards) == shard]",
+     "if owner_of_token(t // block_size, num_shards) == shard]",
+     "token ownership taken per block"),
     ("paged.py", "return j // num_shards", "return (j + 1) // num_shards", "local index off by one"),
     ("paged.py", "return cache[phys, pos % block_size]",
      "return cache[phys, (block_size - 1) - pos % block_size]", "slot reversed in block"),

@@ -40,7 +40,9 @@ import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 PROFILES = ROOT / "profiles"
-KERNEL_SOURCES = ["mla.hip", "gqa.hip", "dcp_internal.hpp"]
+# Sources whose change can move the attention kernel's HBM traffic: the kernels,
+# the work plan that assigns their block ranges, and the launch code.
+KERNEL_SOURCES = ["mla.hip", "gqa.hip", "dcp_internal.hpp", "plan_merge.hip", "api.hip"]
 
 
 def log(msg: str):
@@ -65,10 +67,31 @@ def traffic_from_counters(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, o_gpu, lse_gpu, budget_s: float):
-    """Time the fp64 oracle on a stratified sample of the workload's sequences."""
+def _oracle_pass(w, picks, budget_s, o_gpu=None, lse_gpu=None):
+    """Run the oracle sequence by sequence over `picks` until `budget_s` seconds
+    of oracle time are spent; returns (sequences done, tokens, seconds, errors)."""
     import oracle
-    from threadpoolctl import threadpool_info
+
+    done, tokens, t_used, errs = [], 0, 0.0, []
+    for b in picks:
+        t0 = time.perf_counter()
+        o_ref, lse_ref = oracle.decode_reference(w, batch_indices=[b])
+        t_used += time.perf_counter() - t0
+        done.append(b)
+        tokens += int(w.seq_lens[b])
+        if o_gpu is not None:
+            diff = o_gpu[b].astype(np.float64) - o_ref[b]
+            errs.append((np.linalg.norm(diff) / np.linalg.norm(o_ref[b]), np.abs(diff).max(),
+                         np.abs(lse_gpu[b] - lse_ref[b]).max()))
+        if t_used >= budget_s:
+            break
+    return done, tokens, t_used, errs
+
+
+def cpu_baseline(w, o_gpu, lse_gpu, budget_s: float):
+    """Time the fp64 oracle on a stratified sample of the workload's sequences,
+    with the host's BLAS threads and again on one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     order = np.argsort(w.seq_lens, kind="stable")
     # Stratified over the sorted lengths: passes over every 8th sequence, each pass
@@ -77,28 +100,29 @@ def cpu_baseline(w, o_gpu, lse_gpu, budget_s: float):
     # every sequence was visited.
     picks = [int(order[i]) for off in (4, 0, 6, 2, 5, 1, 7, 3)
              for i in range(off, len(order), 8)]
-    done, tokens, t_used = [], 0, 0.0
-    errs = []
-    for b in picks:
-        t0 = time.perf_counter()
-        o_ref, lse_ref = oracle.decode_reference(w, batch_indices=[b])
-        t_used += time.perf_counter() - t0
-        done.append(b)
-        tokens += int(w.seq_lens[b])
-        diff = o_gpu[b].astype(np.float64) - o_ref[b]
-        errs.append((np.linalg.norm(diff) / np.linalg.norm(o_ref[b]), np.abs(diff).max(),
-                     np.abs(lse_gpu[b] - lse_ref[b]).max()))
-        if t_used >= budget_s:
-            break
+    done, tokens, t_used, errs = _oracle_pass(w, picks, budget_s, o_gpu, lse_gpu)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    kv = tokens * w.spec.kv_bytes_per_token()
+    per_tok = w.spec.kv_bytes_per_token()
+    kv = tokens * per_tok
     rate = kv / t_used / 1e9
     sample = (f"fp64 oracle on {len(done)} of {w.spec.batch} sequences (stratified by length), "
               f"{tokens} tokens = {kv / 1e9:.3f} GB of cached rows in {t_used:.1f} s")
+    # One-thread leg: the same visit order on a third of the budget.
+    with threadpool_limits(limits=1):
+        done1, tokens1, t1, _ = _oracle_pass(w, picks, budget_s / 3)
+    kv1 = tokens1 * per_tok
     parity = {"sequences": len(done), "worst_rel_l2": float(max(e[0] for e in errs)),
               "max_abs": float(max(e[1] for e in errs)), "lse_abs": float(max(e[2] for e in errs))}
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {"value": rate, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": sample}, parity
+            "sample": sample, "host_cpus": os.cpu_count(), "affinity_cpus": affinity,
+            "blas_threads": int(threads),
+            "single_thread": {"value": kv1 / t1 / 1e9, "unit": "GB/s", "cores": 1,
+                              "sample": f"fp64 oracle on one thread, {len(done1)} sequences, "
+                                        f"{tokens1} tokens = {kv1 / 1e9:.3f} GB in {t1:.1f} s"}}, parity
 
 
 def components(dcp, desc, dev, w, ws, iters: int = 20):

@@ -231,7 +231,36 @@ struct Elt<true> {
     for (int i = 0; i < 8; ++i) r[i] = static_cast<_Float16>(static_cast<float>(v[i]));
     return r;
   }
+  // bf16 * 2^-e -> fp16 (the power of two is exact).
+  static __device__ __forceinline__ vec from_bf16_pow2(bf16x8 v, int e) {
+    vec r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      r[i] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(static_cast<float>(v[i]), -e));
+    return r;
+  }
 };
+
+// fp8 caches run both products on fp16 MFMAs, whose operands have a narrow
+// exponent range. Two powers of two keep every finite query and every token
+// scale up to 2^64 inside it, exactly:
+//  * query: each head's query is multiplied by 2^-e with e the exponent of
+//    its largest magnitude (so |q| < 1, and components down to 2^-14 of the
+//    largest keep full precision); the score scale takes 2^e back in fp32;
+//  * probability x scale: a tile's largest token scale is below 2^E (E its
+//    exponent), so p * sigma <= 2^(x_max + E - m) for the tile's largest score
+//    x_max against reference m. Raising the reference on x_max + E rather than
+//    on x_max keeps every fp16 weight p * sigma below 2^kRaise, whatever sigma
+//    is; the fp32 probabilities p (and their sum) take the shift 2^-E, which
+//    stays far inside fp32 for scales in [2^-64, 2^64] (E is clamped at -64 so
+//    that smaller scales cannot push the sum towards overflow).
+__device__ __forceinline__ int max_exponent_head(float amax) {
+  return __builtin_amdgcn_frexp_expf(amax);  // amax < 2^e (0 for amax = 0)
+}
+__device__ __forceinline__ float scale_exponent(float sig_max) {
+  const int e = __builtin_amdgcn_frexp_expf(sig_max);
+  return static_cast<float>(e < -64 ? -64 : e);
+}
 
 // Static configuration: HG groups of 16 heads, 2 * HG waves.
 template <int HG, bool FP8>
@@ -376,11 +405,28 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
 
     // Query fragments (B operand of S^T): head h_s, columns 32kk + 8q4 .. +7.
     typename E::vec qf[kKSteps];
+    float qsl = a.scale_log2;  // score scale (log2 units) of this lane's head
     {
       const uint16_t* qrow = a.q + (static_cast<size_t>(p.b) * a.Hq + h_s) * kQK + 8 * q4;
+      if constexpr (FP8) {
+        // fp16 operands: the head's query scaled by a power of two into (-1, 1)
+        bf16x8 qv[kKSteps];
+        float qm = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk)
-        qf[kk] = E::from_bf16(*reinterpret_cast<const bf16x8*>(qrow + 32 * kk));
+        for (int kk = 0; kk < kKSteps; ++kk) {
+          qv[kk] = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qm = fmaxf(qm, fabsf(static_cast<float>(qv[kk][i])));
+        }
+        const int qe = max_exponent_head(max_xor32(max_xor16(qm)));
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = E::from_bf16_pow2(qv[kk], qe);
+        qsl = __builtin_amdgcn_ldexpf(a.scale_log2, qe);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk)
+          qf[kk] = E::from_bf16(*reinterpret_cast<const bf16x8*>(qrow + 32 * kk));
+      }
     }
     f32x4 acc[kMT][HG];
 #pragma unroll
@@ -616,14 +662,20 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
           wait_lgkm<0>(raw);
           sc4 = __builtin_bit_cast(f32x4, raw);
         }
+        float smax = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * th + 4 * q4 + i;
+          const bool v = (vm_s >> r) & 1ull;
           sig[i] = sc4[i];
-          x[i] = ((vm_s >> r) & 1ull) ? sv[i] * sig[i] * a.scale_log2 : -INFINITY;
+          x[i] = v ? sv[i] * sig[i] * qsl : -INFINITY;
+          smax = fmaxf(smax, v ? fabsf(sig[i]) : 0.f);
         }
         float hmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         hmax = max_xor32(max_xor16(hmax));
+        // fp8: the half's log2 bound of p * sigma against reference 0 (the
+        // reference then rises on it, so every p * sigma stays <= 1)
+        if constexpr (FP8) hmax += scale_exponent(max_xor32(max_xor16(smax)));
         // P^T fragment half of this wave: tokens 16th + 4q4 + i of head h_s.
         auto store_p = [&](const float* pv) -> i32x2 {
           const uint32_t lo = E::pack2(FP8 ? pv[0] * sig[0] : pv[0], FP8 ? pv[1] * sig[1] : pv[1]);
@@ -638,8 +690,8 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
           return add_bf16x2(static_cast<uint32_t>(pk[1]), add_bf16x2(static_cast<uint32_t>(pk[0]), c));
         };
         // bf16 cache: probabilities may reach 2^8 before the reference max of a
-        // head is raised. fp8 cache: it is raised on any increase, so p <= 1
-        // and p * scale stays inside the fp16 range.
+        // head is raised. fp8 cache: it is raised on any increase of the
+        // shifted maximum, so p * scale <= 1.
         constexpr float kRaise = FP8 ? 0.f : 8.f;
         float p[4];
         bool slow = true;
@@ -842,10 +894,9 @@ struct PP {
   static constexpr int kSSpread = kSteps;
   static constexpr int kVSpread = kMT;
   // A head's reference max rises only when a tile's max exceeds it by more
-  // than this (log2 units): probabilities stay <= 2^kRaise. fp8 keeps it at
-  // 4 so that probability times token scale stays inside the fp16 range for
-  // scales below 4096.
-  static constexpr float kRaise = FP8 ? 4.f : 8.f;
+  // than this (log2 units): probabilities (fp8: probability times token scale,
+  // against the shifted reference) stay <= 2^kRaise.
+  static constexpr float kRaise = 8.f;
   static constexpr int kMaxPieces = 32;                      // segments per window
   static constexpr int kMaxTiles = 640;                      // tiles per window
   static constexpr int kPadOff = kStages * kStageB;          // fp8: landing pad of the fillers
@@ -910,6 +961,17 @@ __device__ __forceinline__ i32x4 f8x8_to_f16x8(int d0, int d1) {
                __builtin_bit_cast(int, h3)};
 }
 
+// Buffer resource over `bytes` bytes from `base` (raw 32-bit access, the gfx9
+// family's descriptor word). Loads at offsets at or past `bytes` return zeros
+// without touching memory: a tile's rows past its valid tokens, or every row
+// of a tile whose block id is unusable (bytes = 0), land in LDS as zeros with
+// no per-lane address select.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kOobOff = 0x40000000;  // lane offset past every range (fillers)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufWord3);
+}
+
 // SHARED: several head groups (more than 64 query rows per sequence) stream
 // the same tiles. Their work groups run side by side on one XCD and the copies
 // keep the default cache policy, so the second group finds the tiles in L2.
@@ -948,9 +1010,11 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   // Copies: copy group cw issues slots cw + 8n of a tile. The value waves take
   // the groups with the extra copy (their MFMA loop has more room for them).
   const int cw = (w + 4) & 7;
+  // Every wave issues the same copies for every step, also past the end of a
+  // window (fillers that read nothing), so each wait for a tile's copies is a
+  // constant count.
   const bool hi_wave = cw < P::kHiWaves;
-  int32_t cp_off[P::kPerWave];
-  int cp_row[P::kPerWave];  // tile row this lane's copy n fills
+  int32_t cp_off[P::kPerWave];  // byte offset of this lane's copy n in the tile's rows
 #pragma unroll
   for (int n = 0; n < P::kPerWave; ++n) {
     const int ii = cw + 8 * n;
@@ -966,11 +1030,18 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
       }
     }
     cp_off[n] = static_cast<int32_t>(row * a.token_stride_b) + 16 * c;
-    cp_row[n] = row;
   }
-  auto wait_tiles = [&](int n_after) {
-    if (hi_wave) wait_tiles_after_n<P::kPerWave, kAhead - 1>(n_after);
-    else wait_tiles_after_n<P::kPerWave - 1, kAhead - 1>(n_after);
+  if constexpr (FP8) {
+    // Last round: code rows (cw < kCodeHi), the token scales (cw == kCodeHi:
+    // lanes 0-7 take four tokens each; the others read past the range), or a
+    // filler into the pad.
+    constexpr int n = P::kPerWave - 1;
+    if (cw == P::kCodeHi) cp_off[n] = 16 * lane;
+    else if (cw > P::kCodeHi) cp_off[n] = kOobOff;
+  }
+  auto wait_tiles = [&]() {
+    if (hi_wave) wait_tiles_after_n<P::kPerWave, 1>(kAhead - 1);
+    else wait_tiles_after_n<P::kPerWave - 1, 1>(kAhead - 1);
   };
 
   // Score waves: A fragments of M tile 0 (row l16) and 1 (row 16 + l16).
@@ -1049,47 +1120,53 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
     wait_lgkm<0>(v);
     return wave_uniform(v);
   };
-  // Copy source of a tile: its block's rows (and, for fp8, token scales), and
-  // for rows that hold no real token of a usable block, 16 zero bytes of the
-  // workspace instead (so no tile ever needs zeroing in LDS).
+  // Copy source of a tile: a buffer resource over its valid rows, so rows
+  // without a real token of a usable block read as zeros (no tile is ever
+  // zeroed in LDS), and for fp8 one over the token scales of whole 4-token
+  // chunks (scales of rows past the valid ones are masked by the scores).
+  // A filler (past the window's end) reads nothing.
   struct Src {
-    const char* base;
-    const char* sbase;  // fp8: scale of the tile's first token
-    int nvalid;         // rows taken from the block
+    __amdgpu_buffer_rsrc_t rows;
+    __amdgpu_buffer_rsrc_t last;  // fp8: the last copy round's resource (rows, or the scales)
   };
-  auto tile_src = [&](const TileInfo& ti) -> Src {
-    if (ti.id < 0) return Src{a.kv, a.kv_scale, 0};
+  const unsigned bstride = static_cast<unsigned>(a.block_stride_b);
+  const int tstride = static_cast<int>(a.token_stride_b);
+  auto tile_src = [&](const TileInfo& ti, bool real) -> Src {
+    const bool ok = real && ti.id >= 0;
+    const int nv = ok ? ti.nvalid() : 0;
     const int tok0 = 32 * (ti.y & 0xff);
-    return Src{a.kv + static_cast<long long>(ti.id) * a.block_stride_b +
-                   static_cast<long long>(tok0) * a.token_stride_b,
-               a.kv_scale + 4 * (static_cast<long long>(ti.id) * bs + tok0), ti.nvalid()};
+    const unsigned id = ok ? static_cast<unsigned>(ti.id) : 0u;
+    const __amdgpu_buffer_rsrc_t rows = rows_rsrc(
+        a.kv + (static_cast<unsigned long long>(id) * bstride + static_cast<unsigned>(tok0 * tstride)),
+        nv * tstride);
+    if constexpr (FP8) {
+      if (cw == P::kCodeHi)
+        return Src{rows, rows_rsrc(a.kv_scale + 4 * (static_cast<unsigned long long>(id) * bs + tok0),
+                                   16 * ((nv + 3) >> 2))};
+    }
+    return Src{rows, rows};
   };
   auto copy_one = [&](auto nc, const Src& sr, int t) {
     constexpr int n = decltype(nc)::value;
     const int ii = cw + 8 * n;
     DCP_LDS char* stage = ring + (t % kStages) * P::kStageB;
+    // (Operands bound to locals: with expressions inline in the builtin's
+    // argument list the host pass drops this kernel's stub.)
+    const int off = cp_off[n];
     if constexpr (FP8) {
       if constexpr (n == P::kPerWave - 1) {
-        // Last round: code rows (cw < kCodeHi), the token scales (cw == kCodeHi:
-        // lanes 0-7 take four rows each; rows past nvalid lie in the same block
-        // and are masked by the scores), or a filler into the pad.
-        const bool code = cw < P::kCodeHi;
-        const bool scl = cw == P::kCodeHi;
-        const char* src = a.zero;
-        if (code && cp_row[n] < sr.nvalid) src = sr.base + cp_off[n];
-        if (scl && lane < 8 && 4 * lane < sr.nvalid) src = sr.sbase + 16 * lane;
-        DCP_LDS char* ldst = code ? stage + ii * 1024 : scl ? stage + P::kScaleOff : ring + P::kPadOff;
-        __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, SHARED ? 0 : kCopyPolicy);
+        const __amdgpu_buffer_rsrc_t rs = sr.last;
+        DCP_LDS char* ldst = cw < P::kCodeHi ? stage + ii * 1024
+                             : cw == P::kCodeHi ? stage + P::kScaleOff : ring + P::kPadOff;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ldst, 16, off, 0, 0, SHARED ? 0 : kCopyPolicy);
         return;
       }
     } else {
       if (n == P::kPerWave - 1 && ii >= P::kInst) return;
     }
-    // (Operands bound to locals: with the expressions inline in the
-    // builtin's argument list the host pass drops this kernel's stub.)
-    const char* src = cp_row[n] < sr.nvalid ? sr.base + cp_off[n] : a.zero;
+    const __amdgpu_buffer_rsrc_t rs = sr.rows;
     DCP_LDS char* ldst = stage + ii * 1024;
-    __builtin_amdgcn_global_load_lds(src, ldst, 16, 0, SHARED ? 0 : kCopyPolicy);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ldst, 16, off, 0, 0, SHARED ? 0 : kCopyPolicy);
   };
 
   // The two roles run the same loops and barriers with separate code, so the
@@ -1105,6 +1182,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
 #pragma unroll
     for (int i = 0; i < kSt; ++i) st[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     int qb = -1;
+    float qsl = a.scale_log2;  // fp8: score scale of the loaded query (log2 units)
     auto load_q = [&](int b) {
       // K step kk covers query columns 32kk + 8q4 .. +7 (bf16), or
       // 64(kk / 2) + 16q4 + 8(kk % 2) .. +7 (fp8, the chunk order above).
@@ -1121,9 +1199,19 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
 #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk) asm volatile("" : "+v"(st[kk]));
       if constexpr (FP8) {
+        // The head's largest magnitude over the four lanes that hold it.
+        float qm = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk) {
+          const bf16x8 v = __builtin_bit_cast(bf16x8, st[kk]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qm = fmaxf(qm, fabsf(static_cast<float>(v[i])));
+        }
+        const int qe = max_exponent_head(max_xor32(max_xor16(qm)));
 #pragma unroll
         for (int kk = 0; kk < kKSteps; ++kk)
-          st[kk] = __builtin_bit_cast(f32x4, E::from_bf16(__builtin_bit_cast(bf16x8, st[kk])));
+          st[kk] = __builtin_bit_cast(f32x4, E::from_bf16_pow2(__builtin_bit_cast(bf16x8, st[kk]), qe));
+        qsl = __builtin_amdgcn_ldexpf(a.scale_log2, qe);
       }
       qb = b;
     };
@@ -1226,20 +1314,22 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
       }
       wait_vm<0>();
       __syncthreads();
-      // prologue: the first kAhead tiles (fp8: fillers past the last tile, so
-      // that every step is preceded by the same number of copies)
-      for (int t = 0; t < kAhead && (P::kPipe || t < T); ++t) {
-        const Src sr = t < T ? tile_src(tile_info(t)) : Src{a.kv, a.kv_scale, 0};
+      // prologue: the first kAhead tiles (fillers past the last tile, so that
+      // every step is preceded by the same number of copies)
+      for (int t = 0; t < kAhead; ++t) {
+        const Src sr = tile_src(tile_info(min(t, max(T - 1, 0))), t < T);
         static_for<0, P::kPerWave>([&](auto nc) { copy_one(nc, sr, t); });
       }
 
       // Start of step ks (score waves on tile ks, value waves on tile ks - 1):
-      // this wave's copies of tile ks have landed, then the barrier makes every
-      // wave's copies visible and guarantees that step ks - 1 is finished, so
-      // the stage of tile ks - 2 is free for tile ks + kAhead. Both roles pass
-      // the same barriers in the same order.
-      auto step_begin = [&](int ks) {
-        if (ks < T) wait_tiles(P::kPipe ? kAhead - 1 : min(kAhead - 1, T - 1 - ks));
+      // this wave's copies of tile ks have landed (every step issues one tile,
+      // a filler past the window's end, so kAhead - 1 tiles are in flight
+      // after it), then the barrier makes every wave's copies visible and
+      // guarantees that step ks - 1 is finished, so the stage of tile ks - 2 is
+      // free for tile ks + kAhead. Both roles pass the same barriers in the
+      // same order.
+      auto step_begin = [&](int) {
+        wait_tiles();
         lds_barrier();
       };
 
@@ -1255,6 +1345,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         TileInfo tip{-1, 0};
         f32x4 svp0 = {0.f, 0.f, 0.f, 0.f}, svp1 = svp0;
         i32x4 scp0 = {0, 0, 0, 0}, scp1 = scp0;
+        float qslp = qsl;  // score scale of tile ks - 1's query
         for (int ks = 0; ks <= T; ++ks) {
           step_begin(ks);
           const bool has_s = ks < T;   // step ks scores tile ks ...
@@ -1280,8 +1371,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           // (In the window's last step there is no tile ks: the score loop then
           // reads a stale stage and its results are dropped; the copies are
           // fillers.)
-          const bool do_issue = ks + kAhead < T;
-          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, a.kv_scale, 0};
+          const Src nsrc = tile_src(tiss, ks + kAhead < T);
           const uint32_t tile = ring_addr + (ks % kStages) * P::kStageB;
           i32x4 sc0, sc1;
           lds_b128<0>(sc0, tile + P::kScaleOff + 16 * q4);
@@ -1309,12 +1399,15 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
               const bool v0 = (lo >> i) & 1u, v1 = (hi >> i) & 1u;
               sig[i] = v0 ? __int_as_float(scp0[i]) : 0.f;
               sig[4 + i] = v1 ? __int_as_float(scp1[i]) : 0.f;
-              x[i] = v0 ? svp0[i] * sig[i] * a.scale_log2 : -INFINITY;
-              x[4 + i] = v1 ? svp1[i] * sig[4 + i] * a.scale_log2 : -INFINITY;
+              x[i] = v0 ? svp0[i] * sig[i] * qslp : -INFINITY;
+              x[4 + i] = v1 ? svp1[i] * sig[4 + i] * qslp : -INFINITY;
             }
             float hmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                                fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-            hmax = max_xor32(max_xor16(hmax));
+            float smax = fmaxf(fmaxf(fmaxf(fabsf(sig[0]), fabsf(sig[1])), fmaxf(fabsf(sig[2]), fabsf(sig[3]))),
+                               fmaxf(fmaxf(fabsf(sig[4]), fabsf(sig[5])), fmaxf(fabsf(sig[6]), fabsf(sig[7]))));
+            // log2 bound of this tile's p * sigma against reference 0
+            hmax = max_xor32(max_xor16(hmax)) + scale_exponent(max_xor32(max_xor16(smax)));
             raise = hmax > m_ref + P::kRaise;
             alpha = raise ? fast_exp2(m_ref - hmax) : 1.f;  // 0 when m_ref = -inf
             m_new = raise ? hmax : m_ref;
@@ -1380,6 +1473,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           }
           wait_lgkm<0>(sc0, sc1);
           tip = ti;
+          qslp = qsl;
           svp0 = sv0;
           svp1 = sv1;
           scp0 = sc0;
@@ -1392,8 +1486,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         // makes the register allocator rotate them through fresh registers.)
         for (int ks = 0; ks < 2; ++ks) {
           step_begin(ks);
-          const bool do_issue = ks + kAhead < T;
-          const Src nsrc = do_issue ? tile_src(tile_info(ks + kAhead)) : Src{a.kv, a.kv_scale, 0};
+          const Src nsrc = tile_src(tile_info(min(ks + kAhead, max(T - 1, 0))), ks + kAhead < T);
           static_for<0, P::kPerWave>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
         }
         i32x2 e_kv = {0, 0}, e_iss = {0, 0};
@@ -1403,10 +1496,9 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         }
         for (int ks = 2; ks <= T + 1; ++ks) {
           step_begin(ks);
-          const bool do_issue = ks + kAhead < T;
           const TileInfo tiss = entry_take(e_iss);
           entry_read(e_iss, min(ks + 1 + kAhead, T - 1));
-          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, a.kv_scale, 0};
+          const Src nsrc = tile_src(tiss, ks + kAhead < T);
           const TileInfo ti = entry_take(e_kv);
           entry_read(e_kv, min(ks - 1, T - 1));
           const int kv = ks - 2;
@@ -1507,8 +1599,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             const int b = piece_b(ti.piece());
             if (b != qb) load_q(b);
           }
-          const bool do_issue = ks + kAhead < T;
-          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, a.kv_scale, 0};
+          const Src nsrc = tile_src(tiss, ks + kAhead < T);
           const uint32_t tile = ring_addr + (ks % kStages) * P::kStageB;
           // fp8: the token scales of this lane's score rows 4q4 + i and 16 + 4q4 + i
           i32x4 sc0 = {0, 0, 0, 0}, sc1 = {0, 0, 0, 0};
@@ -1559,7 +1650,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             // copies n in [n0, n1) go out after this read
             constexpr int n0 = kk < P::kSSpread ? kk * P::kPerWave / P::kSSpread : P::kPerWave;
             constexpr int n1 = kk < P::kSSpread ? (kk + 1) * P::kPerWave / P::kSSpread : P::kPerWave;
-            if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
+            static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
           });
           const f32x4 sv0 = s0a + s0b, sv1 = s1a + s1b;
 
@@ -1637,8 +1728,8 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
       } else {
         // Step 0 has no value tile yet: only this wave's copies of tile kAhead.
         step_begin(0);
-        if (kAhead < T) {
-          const Src nsrc = tile_src(tile_info(kAhead));
+        {
+          const Src nsrc = tile_src(tile_info(min(kAhead, max(T - 1, 0))), kAhead < T);
           static_for<0, P::kPerWave>([&](auto nc) { copy_one(nc, nsrc, kAhead); });
         }
         i32x2 e_kv = {0, 0}, e_iss = {0, 0};
@@ -1652,8 +1743,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           const TileInfo tiss = entry_take(e_iss);
           entry_read(e_kv, min(ks, T - 1));
           entry_read(e_iss, min(ks + 1 + kAhead, T - 1));
-          const bool do_issue = ks + kAhead < T;
-          const Src nsrc = do_issue ? tile_src(tiss) : Src{a.kv, a.kv_scale, 0};
+          const Src nsrc = tile_src(tiss, ks + kAhead < T);
           const int kv = ks - 1;
           // LDS reads of this step, oldest first: the rescale votes of tile kv,
           // its P^T fragments, then the first transposed tile fragments; the
@@ -1716,7 +1806,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             });
             constexpr int n0 = mt < P::kVSpread ? mt * P::kPerWave / P::kVSpread : P::kPerWave;
             constexpr int n1 = mt < P::kVSpread ? (mt + 1) * P::kPerWave / P::kVSpread : P::kPerWave;
-            if (do_issue) static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
+            static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
           });
           if (ti.last()) {
             // Segment done: normalise by the score waves' head sums and store
@@ -1771,12 +1861,20 @@ bool mla_supported(const dcp_attn_desc_t* d) {
 
 // The producer/consumer kernel: groups of 64 heads, blocks of a multiple of 32
 // tokens (a tile then lies inside one block, and per-lane copy offsets,
-// row * token stride, fit in 32 bits).
+// row * token stride, fit in 32 bits) and of at most 8192 tokens (the tile
+// table keeps a tile's offset in its block in 8 bits, and a window of
+// kMaxTiles tiles must hold at least one whole block). Larger blocks take the
+// general kernel. A tile's address is block id * block stride (the stride
+// below 4 GiB) plus its offset in the block (the block's rows below 4 GiB).
 // Multi-token decode needs each 64-row head group to hold one query token.
 static bool use_pp(const dcp_attn_desc_t* d) {
   const long long elt = d->kv_dtype == DCP_BF16 ? 2 : 1;
-  return desc_rows(d) >= 64 && d->block_size % kT == 0 &&
+  static_assert(PP<false>::kMaxTiles >= 8192 / kT && PP<true>::kMaxTiles >= 8192 / kT,
+                "a window holds one block of the largest size");
+  return desc_rows(d) >= 64 && d->block_size % kT == 0 && d->block_size <= 8192 &&
          d->kv_token_stride * elt * kT < (1ll << 30) &&
+         d->kv_block_stride * elt < (1ll << 32) &&
+         d->kv_token_stride * elt * d->block_size < (1ll << 32) &&
          (desc_q_len(d) == 1 || d->num_q_heads % 64 == 0);
 }
 

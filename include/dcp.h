@@ -109,8 +109,11 @@ typedef struct {
  *   DCP_KV_LATENT: q BF16; kv BF16, or FP8_E4M3 with kv_scale; qk_dim 576,
  *     v_dim 512; q_len * num_q_heads 16, 32 or a multiple of 64 up to 256
  *     (with q_len > 1, num_q_heads a multiple of 16). With an
- *     FP8 cache the products run in fp16: query values must lie inside the
- *     fp16 range (|q| <= 65504) and scales must not exceed 65504.
+ *     FP8 cache both products run on fp16 MFMAs; each head's query and each
+ *     tile's probability-times-scale weights are brought into fp16's range by
+ *     exact powers of two, so the query may hold any finite values and the
+ *     token scales any finite non-negative values up to 2^64 (nonzero scales
+ *     below 2^-64 keep less than fp16 precision in their weights).
  * Cache rows (the qk_dim / v_dim values of one token and head) must start on
  * a 16-byte boundary. */
 
@@ -190,8 +193,9 @@ dcp_status_t dcp_block_remap_update(const int32_t* block_table, const int32_t* o
  * magnitude, and each code is the nearest E4M3 value (ties to even) of
  * x * (448 / amax), both quotients rounded once in fp32; a row with amax 0
  * (or 448 / amax beyond fp32) is stored as zero codes with sigma = 1. Inputs
- * must be finite. The pages name an FP8 KV cache (section 7) without a rule;
- * this one is a reading.
+ * must be finite; rows with amax above 448 * 2^64 get a scale beyond the
+ * range fp8 decoding supports. The pages name an FP8 KV cache (section 7)
+ * without a rule; this one is a reading.
  * Tokens with a negative position, a sequence outside [0, batch), a block
  * past the table width or a table entry outside [0, num_cache_blocks) are
  * skipped. Two tokens for the same slot in one call race. */

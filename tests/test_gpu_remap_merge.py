@@ -46,7 +46,9 @@ def test_remap_full_size_tables(name):
     assert np.array_equal(lt, rt) and np.array_equal(ll, rl)
 
 
-@pytest.mark.parametrize("ownership", oracle.OWNERSHIPS)
+# Block-level ownerships only: under token-level interleave every block holds
+# tokens of every shard, so there is no per-shard table to remap.
+@pytest.mark.parametrize("ownership", ["interleaved", "contiguous"])
 def test_remap_edges(ownership):
     rng = np.random.default_rng(5)
     for bs in (1, 3, 16, 64):

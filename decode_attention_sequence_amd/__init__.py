@@ -121,6 +121,9 @@ def lib():
         L.dcp_decode_all_shards_timed.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P,
                                                   _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]
         L.dcp_decode_all_shards_timed.restype = _I
+        L.dcp_decode_all_shards_noalloc.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P,
+                                                    _P, _P, _P, _P]
+        L.dcp_decode_all_shards_noalloc.restype = _I
         L.dcp_status_str.argtypes = [_I]
         L.dcp_status_str.restype = ctypes.c_char_p
         L.dcp_version.argtypes = []
@@ -400,6 +403,18 @@ def decode_all_shards(desc: AttnDesc, q, k_cache, v_cache, kv_scale, block_table
             ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_scale),
             _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse_out), _ptr(workspace),
             workspace.numel(), _stream(dev), ev0.handle, ev1.handle))
+    return out, lse_out
+
+
+def decode_all_shards_noalloc(desc: AttnDesc, q, k_cache, v_cache, kv_scale, block_table,
+                              seq_lens, out: torch.Tensor, lse_out: Optional[torch.Tensor] = None):
+    """decode_all_shards without a workspace: the library's static device scratch
+    holds the plan and partials. ``out`` (and ``lse_out``) are the caller's buffers;
+    the call allocates nothing."""
+    _check(lib().dcp_decode_all_shards_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache),
+                                               _ptr(v_cache), _ptr(kv_scale), _ptr(block_table),
+                                               _ptr(seq_lens), _ptr(out), _ptr(lse_out),
+                                               _stream(q.device)))
     return out, lse_out
 
 

@@ -2,6 +2,8 @@
 // carving and the launch sequence plan -> attention -> merge on one stream.
 #include <math.h>
 
+#include <mutex>
+
 #include "dcp_internal.hpp"
 
 using namespace dcp;
@@ -9,6 +11,36 @@ using namespace dcp;
 namespace {
 
 constexpr int32_t kVersion = 100;  // 0.1.0
+
+// Scratch of dcp_decode_all_shards_noalloc: one static device array per GPU.
+// Host code refers to it only through the device address that
+// hipGetSymbolAddress returns with that GPU current (the array's name in host
+// code is a host-side stand-in, not a device address), resolved once per
+// device and kept here.
+__device__ __align__(256) char noalloc_scratch[DCP_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the GPU that runs `stream`.
+dcp_status_t noalloc_scratch_ptr(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return DCP_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DCP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return DCP_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return DCP_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return DCP_ERR_HIP;
+    if (e != hipSuccess || !p) return DCP_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DCP_OK;
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -73,15 +105,15 @@ dcp_status_t run_attention(const dcp_attn_desc_t* d, const void* q, const void* 
                            hipEvent_t attn_begin = nullptr, hipEvent_t attn_end = nullptr) {
   const int G = groups_for(d);
   const int rows = desc_rows(d);
-  const size_t need = workspace_bytes_for(S, G, d->batch, rows, d->v_dim);
+  const bool seq_pieces = d->kv_kind == DCP_KV_LATENT && mla_sequence_pieces(d);
+  const size_t need = workspace_bytes_for(S, G, d->batch, rows, d->v_dim, seq_pieces);
   SegMap m = map;
   // No cache blocks: every block id is unusable, so every sequence is empty.
   if (d->num_cache_blocks == 0) m.width = 0;
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
-  WorkspaceView ws = carve_workspace(workspace, S, G, d->batch, rows, d->v_dim);
+  WorkspaceView ws = carve_workspace(workspace, S, G, d->batch, rows, d->v_dim, seq_pieces);
   // Fixed work per piece of a segment, in blocks (about 128 tokens' worth).
   const int seg_cost = (128 + d->block_size - 1) / d->block_size;
-  const bool seq_pieces = d->kv_kind == DCP_KV_LATENT && mla_sequence_pieces(d);
   if (launch_plan(m, S, G, seg_cost, rows, seq_pieces, ws, stream) != hipSuccess)
     return DCP_ERR_HIP;
   AttnLaunch L{d, q, k, v, kv_scale, m, S, ws, cz};
@@ -142,8 +174,9 @@ size_t dcp_workspace_size(const dcp_attn_desc_t* d) {
   if (check_desc(d) != DCP_OK) return 0;
   const int G = groups_for(d);
   const int S_all = d->batch * d->num_shards;
-  const size_t a = workspace_bytes_for(S_all, G, d->batch, desc_rows(d), d->v_dim);
-  const size_t b = workspace_bytes_for(d->batch, G, d->batch, desc_rows(d), d->v_dim);
+  const bool sp = d->kv_kind == DCP_KV_LATENT && mla_sequence_pieces(d);
+  const size_t a = workspace_bytes_for(S_all, G, d->batch, desc_rows(d), d->v_dim, sp);
+  const size_t b = workspace_bytes_for(d->batch, G, d->batch, desc_rows(d), d->v_dim, sp);
   return a > b ? a : b;
 }
 
@@ -267,6 +300,24 @@ dcp_status_t dcp_decode_all_shards(const dcp_attn_desc_t* d, const void* q, cons
                                    hipStream_t stream) {
   return dcp_decode_all_shards_timed(d, q, k_cache, v_cache, kv_scale, block_table, seq_lens, out,
                                      lse_out, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+dcp_status_t dcp_decode_all_shards_noalloc(const dcp_attn_desc_t* d, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const float* kv_scale, const int32_t* block_table,
+                                           const int32_t* seq_lens, void* out, float* lse_out,
+                                           hipStream_t stream) {
+  dcp_status_t st = check_desc(d);
+  if (st != DCP_OK) return st;
+  const bool sp = d->kv_kind == DCP_KV_LATENT && mla_sequence_pieces(d);
+  const size_t need = workspace_bytes_for(d->batch * d->num_shards, groups_for(d), d->batch,
+                                          desc_rows(d), d->v_dim, sp);
+  if (need > DCP_NOALLOC_SCRATCH_BYTES) return DCP_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if ((st = noalloc_scratch_ptr(stream, &scratch)) != DCP_OK) return st;
+  return dcp_decode_all_shards_timed(d, q, k_cache, v_cache, kv_scale, block_table, seq_lens, out,
+                                     lse_out, scratch, DCP_NOALLOC_SCRATCH_BYTES, stream, nullptr,
+                                     nullptr);
 }
 
 dcp_status_t dcp_decode_all_shards_timed(const dcp_attn_desc_t* d, const void* q,

@@ -186,8 +186,10 @@ struct WorkspaceView {
   int num_slots;
 };
 
-size_t workspace_bytes_for(int S, int G, int B, int Hq, int v_dim);
-WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim);
+// Partial slots of a launch: one per (work group, segment) piece, S + G - 1;
+// with sequence pieces (one partial per work group and sequence), B + G - 1.
+size_t workspace_bytes_for(int S, int G, int B, int Hq, int v_dim, bool seq_pieces);
+WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim, bool seq_pieces);
 
 hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, int Hq, bool seq_pieces,
                        WorkspaceView ws, hipStream_t stream);

@@ -20,18 +20,22 @@ static inline size_t plan_bytes(int S, int G, int B) {
                                                  static_cast<size_t>(G) + 1 + 2 * static_cast<size_t>(B));
 }
 
-size_t workspace_bytes_for(int S, int G, int B, int Hq, int v_dim) {
-  size_t slots = static_cast<size_t>(S) + static_cast<size_t>(G) - 1;
+static inline int slot_count(int S, int G, int B, bool seq_pieces) {
+  return (seq_pieces ? B : S) + G - 1;
+}
+
+size_t workspace_bytes_for(int S, int G, int B, int Hq, int v_dim, bool seq_pieces) {
+  size_t slots = static_cast<size_t>(slot_count(S, G, B, seq_pieces));
   size_t off = align_up(plan_bytes(S, G, B), 256);
   off += align_up(slots * Hq * sizeof(float), 256);
   off += slots * Hq * v_dim * sizeof(float);
   return off;
 }
 
-WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim) {
+WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim, bool seq_pieces) {
   WorkspaceView v;
   char* base = static_cast<char*>(ws);
-  v.num_slots = S + G - 1;
+  v.num_slots = slot_count(S, G, B, seq_pieces);
   v.header = reinterpret_cast<PlanHeader*>(base);
   v.seg_off = reinterpret_cast<int32_t*>(base + sizeof(PlanHeader));
   v.cost_off = v.seg_off + S + 1;

@@ -296,6 +296,27 @@ dcp_status_t dcp_decode_all_shards_timed(const dcp_attn_desc_t* desc, const void
                                          hipStream_t stream, hipEvent_t attn_begin,
                                          hipEvent_t attn_end);
 
+/* Bytes of the device scratch array behind dcp_decode_all_shards_noalloc. */
+#define DCP_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* dcp_decode_all_shards for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops that must not allocate, harnesses
+ * that forbid it. Same computation and arguments without the workspace; the
+ * work plan and split partials go to a static device array of
+ * DCP_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends (its address is resolved once per device, on the
+ * first call there). The call itself allocates nothing.
+ * Returns DCP_ERR_WORKSPACE when the descriptor needs more scratch than that
+ * (the need is at most dcp_workspace_size(desc); the batch-64 and batch-128
+ * absorbed-MLA shapes with 64 heads need about 42 and 50 MiB).
+ * Every call on one GPU shares that GPU's array: calls ordered on one stream
+ * are safe, calls that may overlap (other streams, other threads) race. */
+dcp_status_t dcp_decode_all_shards_noalloc(const dcp_attn_desc_t* desc, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const float* kv_scale, const int32_t* block_table,
+                                           const int32_t* seq_lens, void* out, float* lse_out,
+                                           hipStream_t stream);
+
 /* Static text for a status code. */
 const char* dcp_status_str(dcp_status_t status);
 

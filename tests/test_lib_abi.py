@@ -88,8 +88,11 @@ def test_valid_descriptors_have_a_workspace():
     for d in (mla_desc(), mla_desc(kv_dtype=dcp.FP8_E4M3, kv_block_stride=64 * 576),
               gqa_desc(), gqa_desc(q_dtype=dcp.F32, kv_dtype=dcp.F32)):
         n = dcp.lib().dcp_workspace_size(ctypes.byref(d))
-        # At least one partial slot per (sequence, shard) of fp32 output.
-        assert n >= d.batch * d.num_shards * d.num_q_heads * (d.v_dim + 1) * 4
+        # At least one partial slot (fp32 output and LSE) per sequence: the
+        # 64-head latent kernel keeps one partial per work group and sequence,
+        # the others one per work group and (sequence, shard).
+        per = d.batch if d.kv_kind == dcp.KV_LATENT else d.batch * d.num_shards
+        assert n >= per * d.num_q_heads * (d.v_dim + 1) * 4
 
 
 INVALID = [

@@ -113,6 +113,9 @@ def lib():
         L.dcp_decode_partial_mtp.argtypes = [ctypes.POINTER(AttnDesc), _I, _P, _P, _P, _P, _P,
                                              _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.dcp_decode_partial_mtp.restype = _I
+        L.dcp_decode_partial_token.argtypes = [ctypes.POINTER(AttnDesc), _I, _P, _P, _P, _P, _P,
+                                               _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.dcp_decode_partial_token.restype = _I
         L.dcp_lse_merge.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]
         L.dcp_lse_merge.restype = _I
         L.dcp_decode_all_shards.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P,
@@ -353,6 +356,27 @@ def decode_partial_mtp(desc: AttnDesc, shard: int, q_pos: torch.Tensor, q, k_cac
                                         _ptr(local_block_table), _ptr(local_seq_lens),
                                         _ptr(o_partial), _ptr(lse_partial), _ptr(workspace),
                                         workspace.numel(), _stream(dev)))
+    return o_partial, lse_partial
+
+
+def decode_partial_token(desc: AttnDesc, shard: int, q, k_cache, v_cache, kv_scale, block_table,
+                         seq_lens, workspace: Optional[torch.Tensor] = None,
+                         o_partial: Optional[torch.Tensor] = None,
+                         lse_partial: Optional[torch.Tensor] = None):
+    """One shard's partial under token-level interleave (position t on shard
+    t % D), over the global table and lengths: (O_r [B, Hq, v_dim], LSE_r [B, Hq])."""
+    dev = q.device
+    if workspace is None:
+        workspace = alloc_workspace(desc, dev)
+    rows = _rows(desc)
+    if o_partial is None:
+        o_partial = torch.empty((desc.batch, rows, desc.v_dim), dtype=torch.float32, device=dev)
+    if lse_partial is None:
+        lse_partial = torch.empty((desc.batch, rows), dtype=torch.float32, device=dev)
+    _check(lib().dcp_decode_partial_token(ctypes.byref(desc), int(shard), _ptr(q), _ptr(k_cache),
+                                          _ptr(v_cache), _ptr(kv_scale), _ptr(block_table),
+                                          _ptr(seq_lens), _ptr(o_partial), _ptr(lse_partial),
+                                          _ptr(workspace), workspace.numel(), _stream(dev)))
     return o_partial, lse_partial
 
 

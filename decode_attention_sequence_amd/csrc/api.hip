@@ -98,14 +98,17 @@ dcp_status_t check_tensors(const dcp_attn_desc_t* d, const void* q, const void* 
   return DCP_OK;
 }
 
+// scale_ts: token stride of the fp8 scales (a token-interleave view's shard
+// count; else 1), scale_bs: their block stride in tokens (0: the block size).
 dcp_status_t run_attention(const dcp_attn_desc_t* d, const void* q, const void* k, const void* v,
                            const float* kv_scale, const SegMap& map, int S, const Causal& cz,
                            void* out, dcp_dtype_t out_dtype, float* lse_out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream,
-                           hipEvent_t attn_begin = nullptr, hipEvent_t attn_end = nullptr) {
+                           hipEvent_t attn_begin = nullptr, hipEvent_t attn_end = nullptr,
+                           int scale_ts = 1, int scale_bs = 0) {
   const int G = groups_for(d);
   const int rows = desc_rows(d);
-  const bool seq_pieces = d->kv_kind == DCP_KV_LATENT && mla_sequence_pieces(d);
+  const bool seq_pieces = d->kv_kind == DCP_KV_LATENT && mla_sequence_pieces(d, scale_ts);
   const size_t need = workspace_bytes_for(S, G, d->batch, rows, d->v_dim, seq_pieces);
   SegMap m = map;
   // No cache blocks: every block id is unusable, so every sequence is empty.
@@ -116,7 +119,7 @@ dcp_status_t run_attention(const dcp_attn_desc_t* d, const void* q, const void* 
   const int seg_cost = (128 + d->block_size - 1) / d->block_size;
   if (launch_plan(m, S, G, seg_cost, rows, seq_pieces, ws, stream) != hipSuccess)
     return DCP_ERR_HIP;
-  AttnLaunch L{d, q, k, v, kv_scale, m, S, ws, cz};
+  AttnLaunch L{d, q, k, v, kv_scale, m, S, ws, cz, scale_bs > 0 ? scale_bs : d->block_size, scale_ts};
   if (attn_begin && hipEventRecord(attn_begin, stream) != hipSuccess) return DCP_ERR_HIP;
   hipError_t err = d->kv_kind == DCP_KV_LATENT ? launch_mla(L, stream) : launch_gqa(L, stream);
   if (err != hipSuccess) return DCP_ERR_HIP;
@@ -148,6 +151,8 @@ dcp_status_t shard_partial(const dcp_attn_desc_t* d, int shard, const int32_t* q
   map.D = 1;
   map.bs = d->block_size;
   map.batch = d->batch;
+  map.tok_r = 0;
+  map.tok_D = 1;
   Causal cz{q_pos, q_pos ? desc_q_len(d) : 1, d->num_q_heads, shard, d->num_shards};
   return run_attention(d, q, k_cache, v_cache, kv_scale, map, d->batch, cz, o_partial, DCP_F32,
                        lse_partial, workspace, workspace_bytes, stream);
@@ -276,6 +281,48 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* d, int32_t shard, con
                        local_seq_lens, o_partial, lse_partial, workspace, workspace_bytes, stream);
 }
 
+dcp_status_t dcp_decode_partial_token(const dcp_attn_desc_t* d, int32_t shard, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const float* kv_scale, const int32_t* block_table,
+                                      const int32_t* seq_lens, float* o_partial,
+                                      float* lse_partial, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  dcp_status_t st = check_desc(d);
+  if (st != DCP_OK) return st;
+  if (desc_q_len(d) > 1 || shard < 0 || shard >= d->num_shards) return DCP_ERR_INVALID_ARG;
+  if ((st = check_tensors(d, q, k_cache, v_cache, kv_scale)) != DCP_OK) return st;
+  if (!block_table || !seq_lens || !o_partial || !lse_partial) return DCP_ERR_INVALID_ARG;
+  if (!aligned(o_partial, 16)) return DCP_ERR_INVALID_ARG;
+  const int D = d->num_shards;
+  if (d->block_size % D) return DCP_ERR_UNSUPPORTED;
+  if (d->batch == 0) return DCP_OK;
+  // Shard r's view of the cache: every global block holds bs / D of its tokens,
+  // at slots r, r + D, ..., i.e. a cache of blocks of bs / D tokens whose rows
+  // start r tokens in and lie D token strides apart.
+  dcp_attn_desc_t v = *d;
+  v.block_size = d->block_size / D;
+  v.kv_token_stride = d->kv_token_stride * D;
+  v.num_shards = 1;
+  v.max_seq_len = (d->max_seq_len + D - 1) / D;
+  const size_t shift = static_cast<size_t>(shard) * d->kv_token_stride * elt_bytes(d->kv_dtype);
+  const bool pool = d->num_cache_blocks > 0;
+  const void* k = pool ? static_cast<const char*>(k_cache) + shift : k_cache;
+  const void* vc = pool && v_cache ? static_cast<const char*>(v_cache) + shift : v_cache;
+  const float* sc = pool && kv_scale ? kv_scale + shard : kv_scale;
+  SegMap map;
+  map.table = block_table;
+  map.lens = seq_lens;
+  map.width = d->max_blocks_per_seq;
+  map.D = 1;
+  map.bs = v.block_size;
+  map.batch = d->batch;
+  map.tok_r = shard;
+  map.tok_D = D;
+  const Causal cz{nullptr, 1, d->num_q_heads, 0, 1};
+  return run_attention(&v, q, k, vc, sc, map, d->batch, cz, o_partial, DCP_F32, lse_partial,
+                       workspace, workspace_bytes, stream, nullptr, nullptr, D, d->block_size);
+}
+
 dcp_status_t dcp_lse_merge(const float* o_partials, const float* lse_partials,
                            int32_t num_partials, int32_t batch, int32_t num_heads, int32_t v_dim,
                            void* out, dcp_dtype_t out_dtype, float* lse_out, hipStream_t stream) {
@@ -340,6 +387,8 @@ dcp_status_t dcp_decode_all_shards_timed(const dcp_attn_desc_t* d, const void* q
   map.D = d->num_shards;
   map.bs = d->block_size;
   map.batch = d->batch;
+  map.tok_r = 0;
+  map.tok_D = 1;
   const Causal cz{nullptr, desc_q_len(d), d->num_q_heads, 0, 1};
   return run_attention(d, q, k_cache, v_cache, kv_scale, map, d->batch * d->num_shards, cz, out,
                        d->out_dtype, lse_out, workspace, workspace_bytes, stream, attn_begin,

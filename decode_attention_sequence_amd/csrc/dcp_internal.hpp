@@ -57,14 +57,22 @@ struct SegMap {
   int32_t D;             // segments per sequence
   int32_t bs;            // block size
   int32_t batch;
+  // Token-level interleave ("vLLM长序列推理优化", section 2.2): one shard's
+  // view of a global cache, shard tok_r of tok_D holding the positions
+  // t = tok_r + tok_D * i. Its blocks are the global blocks with bs the global
+  // block size / tok_D, and lens are global lengths, of which the shard holds
+  // ceil((L - tok_r) / tok_D). tok_D = 1: lens are the tokens themselves.
+  int32_t tok_r;
+  int32_t tok_D;
 };
 
 // Tokens of sequence b, clamped to what its table row can address.
 __device__ __forceinline__ int seq_tokens(const SegMap& m, int b) {
   int L = m.lens[b];
-  int cap = m.width * m.bs;
-  L = L < 0 ? 0 : L;
-  return L > cap ? cap : L;
+  const long long cap = static_cast<long long>(m.width) * m.bs * m.tok_D;
+  L = L < 0 ? 0 : (L > cap ? static_cast<int>(cap) : L);
+  if (m.tok_D > 1) L = L > m.tok_r ? (L - m.tok_r + m.tok_D - 1) / m.tok_D : 0;
+  return L;
 }
 
 __device__ __forceinline__ int segment_blocks(const SegMap& m, int s) {
@@ -243,6 +251,10 @@ struct AttnLaunch {
   int S;
   WorkspaceView ws;
   Causal cz;
+  // fp8 scale of slot j of block id: kv_scale[id * scale_bs + scale_ts * j]
+  // (scale_bs = block size, scale_ts = 1, except for a token-interleave view)
+  int scale_bs;
+  int scale_ts;
 };
 
 // Query tokens per sequence and query rows per sequence of a descriptor (a
@@ -260,7 +272,8 @@ int gqa_groups(const dcp_attn_desc_t* desc);
 bool mla_supported(const dcp_attn_desc_t* desc);
 // True when the MLA kernel for desc keeps one partial per work group and
 // sequence (slot b + g) rather than one per work group and segment (slot s + g).
-bool mla_sequence_pieces(const dcp_attn_desc_t* desc);
+// scale_ts: token stride of the fp8 scales (1 except in a token-interleave view).
+bool mla_sequence_pieces(const dcp_attn_desc_t* desc, int scale_ts = 1);
 bool gqa_supported(const dcp_attn_desc_t* desc);
 hipError_t launch_mla(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_gqa(const AttnLaunch& a, hipStream_t stream);

@@ -79,7 +79,8 @@ __device__ __forceinline__ int chunk_off(int r, int c) {
 struct MlaArgs {
   const uint16_t* q;      // [B, Hq, 576] bf16 bits
   const char* kv;         // latent cache base
-  const char* kv_scale;   // fp8: fp32 [num_cache_blocks, bs]
+  const char* kv_scale;   // fp8: fp32, scale of slot j of block id at id * scale_bs + scale_ts * j
+  int scale_bs, scale_ts;
   SegMap map;
   const PlanHeader* hdr;
   const int32_t* wg_start;  // [G + 1] block range of each work group
@@ -542,7 +543,8 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
           const int tau = tau0 + (lane & 31);
           const int id = tau < ntok ? ids[tau / bs] : -1;
           const char* src = a.kv_scale;
-          if (id >= 0 && id < a.ncb) src += 4 * (static_cast<long long>(id) * bs + tau % bs);
+          if (id >= 0 && id < a.ncb)
+            src += 4 * (static_cast<long long>(id) * a.scale_bs + static_cast<long long>(a.scale_ts) * (tau % bs));
           __builtin_amdgcn_global_load_lds(
               src, w == 0 ? ring + C::kScaleOff + (j % kStages) * 256 : pad, 4, 0, 0);
         }
@@ -1141,7 +1143,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         nv * tstride);
     if constexpr (FP8) {
       if (cw == P::kCodeHi)
-        return Src{rows, rows_rsrc(a.kv_scale + 4 * (static_cast<unsigned long long>(id) * bs + tok0),
+        return Src{rows, rows_rsrc(a.kv_scale + 4 * (static_cast<unsigned long long>(id) * a.scale_bs + tok0),
                                    16 * ((nv + 3) >> 2))};
     }
     return Src{rows, rows};
@@ -1878,8 +1880,10 @@ static bool use_pp(const dcp_attn_desc_t* d) {
          (desc_q_len(d) == 1 || d->num_q_heads % 64 == 0);
 }
 
-bool mla_sequence_pieces(const dcp_attn_desc_t* d) {
-  return d->kv_kind == DCP_KV_LATENT && use_pp(d);
+// (The producer/consumer kernel copies four consecutive fp8 token scales per
+// lane, so a strided scale view takes the general kernel.)
+bool mla_sequence_pieces(const dcp_attn_desc_t* d, int scale_ts) {
+  return d->kv_kind == DCP_KV_LATENT && use_pp(d) && (d->kv_dtype != DCP_FP8_E4M3 || scale_ts == 1);
 }
 
 template <int HG, bool FP8>
@@ -1896,6 +1900,8 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   a.q = static_cast<const uint16_t*>(L.q);
   a.kv = static_cast<const char*>(L.k_cache);
   a.kv_scale = reinterpret_cast<const char*>(L.kv_scale);
+  a.scale_bs = L.scale_bs;
+  a.scale_ts = L.scale_ts;
   a.map = L.map;
   a.hdr = L.ws.header;
   a.wg_start = L.ws.wg_start;
@@ -1918,7 +1924,7 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   const bool bs32 = d->block_size % kT == 0 && a.token_stride_b * kT < (1ll << 30);
   const int heads = a.Hq < 64 ? a.Hq : 64;
   const dim3 grid(kGroups, a.Hq / heads);
-  if (use_pp(d)) {
+  if (mla_sequence_pieces(d, L.scale_ts)) {
     const int ngrp = a.Hq / 64;
     const dim3 pgrid(kGroups * ngrp);
     if (ngrp > 1) {

@@ -254,6 +254,30 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t shard,
                                     float* lse_partial, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* One shard's partial under token-level interleave, the finer split that
+ * "vLLM长序列推理优化" sets beside block-level ownership (section 2.2; its
+ * section 3.4 lists rank 0 holding positions 0, 4, 8, ... at D = 4): the token
+ * at position t belongs to shard t % num_shards. Every block then holds tokens
+ * of every shard, so the shard reads the global table directly: within each
+ * block its tokens are the slots shard, shard + D, ... (block_size must be a
+ * multiple of num_shards, else DCP_ERR_UNSUPPORTED). Merging the D partials
+ * with dcp_lse_merge gives the unsharded result, as under block ownership.
+ *   shard       this shard's index in [0, num_shards)
+ *   block_table [batch, max_blocks_per_seq] int32 (global)
+ *   seq_lens    [batch] int32 (global lengths; the shard holds
+ *               ceil((L - shard) / num_shards) tokens of a sequence of L)
+ *   o_partial   [batch, num_q_heads, v_dim] fp32 (out)
+ *   lse_partial [batch, num_q_heads] fp32 (out); a shard holding no token of
+ *               a sequence gives O = 0, LSE = -inf
+ * desc->q_len must be at most 1. The workspace is sized by
+ * dcp_workspace_size(desc). Other arguments as in dcp_decode_partial. */
+dcp_status_t dcp_decode_partial_token(const dcp_attn_desc_t* desc, int32_t shard, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const float* kv_scale, const int32_t* block_table,
+                                      const int32_t* seq_lens, float* o_partial,
+                                      float* lse_partial, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
 /* LSE merge of num_partials partial results (summary section of the DCP blog
  * page, merge equation; the reweighting inside cp_lse_ag_out_rs of section A2):
  *   o_partials   [num_partials, batch, num_heads, v_dim] fp32

@@ -239,3 +239,21 @@ def test_status_strings_and_version():
     assert dcp.status_str(0) == "ok"
     assert "workspace" in dcp.status_str(3)
     assert dcp.version() >= 100
+
+
+def call_partial_token(desc, shard, ws_bytes=1 << 40):
+    return dcp.lib().dcp_decode_partial_token(ctypes.byref(desc), shard, FAKE, FAKE, FAKE, FAKE,
+                                              FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def test_token_partial_argument_errors():
+    """Token-level interleave: blocks must split evenly over the shards, the shard
+    index must be in range and the call is single-token; all rejected on the host
+    before anything is enqueued."""
+    assert call_partial_token(mla_desc(block_size=64, num_shards=3,
+                                       max_blocks_per_seq=12024), 0) == dcp.DCP_ERR_UNSUPPORTED
+    assert call_partial_token(gqa_desc(num_shards=3), 1) == dcp.DCP_ERR_UNSUPPORTED
+    assert call_partial_token(mla_desc(), -1) == dcp.DCP_ERR_INVALID_ARG
+    assert call_partial_token(mla_desc(), 8) == dcp.DCP_ERR_INVALID_ARG
+    assert call_partial_token(mla_desc(q_len=2), 0) == dcp.DCP_ERR_INVALID_ARG
+    assert call_partial_token(mla_desc(), 0, ws_bytes=16) == dcp.DCP_ERR_WORKSPACE

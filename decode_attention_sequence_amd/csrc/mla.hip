@@ -169,6 +169,31 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Maxima of operands that are never NaN (finite scores, or -inf for masked
+// rows): plain v_max / v_max3, without the canonicalising maxes the compiler
+// puts in front of fmaxf.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax8(const float* x) {
+  return vmax3(vmax3(x[0], x[1], x[2]), vmax3(x[3], x[4], x[5]), vmax(x[6], x[7]));
+}
+__device__ __forceinline__ float vmax_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float vmax_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // A value every lane holds identically, moved to a scalar register.
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -877,11 +902,14 @@ struct PP {
   static constexpr int kStages = FP8 ? 7 : 4;                // ring stages
   static constexpr int kAhead = kStages - (kPipe ? 3 : 2);   // tiles copied ahead of the scores
   static constexpr int kMT = 8;                              // 16-column M tiles per value wave
-  static constexpr int kPerWave = (kInst + 7) / 8;           // copy rounds per tile (at most)
+  // Waves that issue the tile copies: bf16, the four value waves (the score
+  // waves' instruction stream is the longer one); fp8, all eight.
+  static constexpr int kCopyWaves = FP8 ? 8 : 4;
+  static constexpr int kPerWave = (kInst + kCopyWaves - 1) / kCopyWaves;  // copy rounds per tile
   // Copy groups cw < kCodeHi issue kPerWave code copies per tile, the others
   // one fewer (bf16). fp8: group kCodeHi copies the token scales instead and
   // the remaining groups a filler, so every wave issues kPerWave copies.
-  static constexpr int kCodeHi = kInst % 8 ? kInst % 8 : 8;
+  static constexpr int kCodeHi = kInst % kCopyWaves ? kInst % kCopyWaves : kCopyWaves;
   static constexpr int kHiWaves = FP8 ? 8 : kCodeHi;         // groups with kPerWave operations
   static constexpr int kSmAt = 2;                            // fp8: softmax after this score read
   static constexpr int kSteps = FP8 ? kKSteps / 2 : kKSteps;    // score fragment reads per M tile
@@ -1011,7 +1039,8 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
 
   // Copies: copy group cw issues slots cw + 8n of a tile. The value waves take
   // the groups with the extra copy (their MFMA loop has more room for them).
-  const int cw = (w + 4) & 7;
+  const int cw = FP8 ? (w + 4) & 7 : w - 4;
+  const bool copier = FP8 || !scorer;
   // Every wave issues the same copies for every step, also past the end of a
   // window (fillers that read nothing), so each wait for a tile's copies is a
   // constant count.
@@ -1019,9 +1048,9 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   int32_t cp_off[P::kPerWave];  // byte offset of this lane's copy n in the tile's rows
 #pragma unroll
   for (int n = 0; n < P::kPerWave; ++n) {
-    const int ii = cw + 8 * n;
+    const int ii = cw + P::kCopyWaves * n;
     int row = 0, c = 0;
-    if (ii < P::kInst) {
+    if (copier && ii < P::kInst) {
       if constexpr (FP8) {
         const int slot = ii * 64 + lane;
         row = slot / kF8RowCh;
@@ -1042,6 +1071,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
     else if (cw > P::kCodeHi) cp_off[n] = kOobOff;
   }
   auto wait_tiles = [&]() {
+    if (!copier) return;
     if (hi_wave) wait_tiles_after_n<P::kPerWave, 1>(kAhead - 1);
     else wait_tiles_after_n<P::kPerWave - 1, 1>(kAhead - 1);
   };
@@ -1150,7 +1180,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   };
   auto copy_one = [&](auto nc, const Src& sr, int t) {
     constexpr int n = decltype(nc)::value;
-    const int ii = cw + 8 * n;
+    const int ii = cw + P::kCopyWaves * n;
     DCP_LDS char* stage = ring + (t % kStages) * P::kStageB;
     // (Operands bound to locals: with expressions inline in the builtin's
     // argument list the host pass drops this kernel's stub.)
@@ -1214,6 +1244,17 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         for (int kk = 0; kk < kKSteps; ++kk)
           st[kk] = __builtin_bit_cast(f32x4, E::from_bf16_pow2(__builtin_bit_cast(bf16x8, st[kk]), qe));
         qsl = __builtin_amdgcn_ldexpf(a.scale_log2, qe);
+      } else {
+        // The scale's sign goes into the query (an exact sign flip), so the
+        // scores are multiplied by c = |scale| log2(e). A zero scale is taken
+        // as 2^-100 (every probability then rounds to exactly 1, as for 0),
+        // so that c is positive and -inf scores of masked rows stay -inf.
+        if (a.scale_log2 < 0.f) {
+#pragma unroll
+          for (int kk = 0; kk < kKSteps; ++kk)
+            st[kk] = __builtin_bit_cast(f32x4, __builtin_bit_cast(i32x4, st[kk]) ^ static_cast<int>(0x80008000u));
+        }
+        qsl = fmaxf(fabsf(a.scale_log2), 0x1p-100f);
       }
       qb = b;
     };
@@ -1320,7 +1361,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
       // every step is preceded by the same number of copies)
       for (int t = 0; t < kAhead; ++t) {
         const Src sr = tile_src(tile_info(min(t, max(T - 1, 0))), t < T);
-        static_for<0, P::kPerWave>([&](auto nc) { copy_one(nc, sr, t); });
+        if (copier) static_for<0, P::kPerWave>([&](auto nc) { copy_one(nc, sr, t); });
       }
 
       // Start of step ks (score waves on tile ks, value waves on tile ks - 1):
@@ -1580,40 +1621,30 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
         }
        }
       } else if constexpr (kScorer) {
-        i32x2 e_cur = {0, 0}, e_iss = {0, 0};
-        if (T > 0) {
-          entry_read(e_cur, 0);
-          entry_read(e_iss, min(kAhead, T - 1));
-        }
+        // bf16 score waves (fp8 caches take the pipelined branch above). They
+        // issue no copies: the value waves copy the tiles.
+        static_assert(!FP8, "fp8 score waves are pipelined");
+        i32x2 e_cur = {0, 0};
+        if (T > 0) entry_read(e_cur, 0);
         for (int ks = 0; ks < T; ++ks) {
           step_begin(ks);
           const TileInfo ti = entry_take(e_cur);
-          const TileInfo tiss = entry_take(e_iss);
           entry_read(e_cur, min(ks + 1, T - 1));
-          entry_read(e_iss, min(ks + 1 + kAhead, T - 1));
           if (ti.first()) {
             m_ref = -INFINITY;
             l_run = 0.f;
             l_rnd = 0.f;
             // A new sequence needs its query. (Loaded here, in the iteration
-            // that uses it, the compiler's waits for it are exact and do not
-            // drain the copies in flight.)
+            // that uses it, the compiler's waits for it are exact.)
             const int b = piece_b(ti.piece());
             if (b != qb) load_q(b);
           }
-          const Src nsrc = tile_src(tiss, ks + kAhead < T);
           const uint32_t tile = ring_addr + (ks % kStages) * P::kStageB;
-          // fp8: the token scales of this lane's score rows 4q4 + i and 16 + 4q4 + i
-          i32x4 sc0 = {0, 0, 0, 0}, sc1 = {0, 0, 0, 0};
-          if constexpr (FP8) {
-            lds_b128<0>(sc0, tile + P::kScaleOff + 16 * q4);
-            lds_b128<64>(sc1, tile + P::kScaleOff + 16 * q4);
-          }
           i32x4 ra[P::kSRing], rb[P::kSRing];
           auto s_issue = [&](auto kc) {
             constexpr int kk = decltype(kc)::value;
-            constexpr int off = FP8 ? 64 * kk : 128 * (kk >> 1);
-            if constexpr (!FP8 && (kk & 1)) {
+            constexpr int off = 128 * (kk >> 1);
+            if constexpr (kk & 1) {
               lds_b128<off>(ra[kk % P::kSRing], tile + a0o);
               lds_b128<off>(rb[kk % P::kSRing], tile + a1o);
             } else {
@@ -1628,95 +1659,59 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             if constexpr (kk + P::kSDist < P::kSteps) s_issue(IC<kk + P::kSDist>{});
             constexpr int ahead = kk + P::kSDist < P::kSteps ? P::kSDist : P::kSteps - 1 - kk;
             wait_lgkm<2 * ahead>(ra[kk % P::kSRing], rb[kk % P::kSRing]);
-            if constexpr (FP8) {
-              // read kk: K steps 2kk (codes 0-7) and 2kk + 1 (codes 8-15)
-              const i32x4 ua = ra[kk % P::kSRing], ub = rb[kk % P::kSRing];
-              const i32x4 a00 = f8x8_to_f16x8(ua[0], ua[1]), a01 = f8x8_to_f16x8(ua[2], ua[3]);
-              const i32x4 a10 = f8x8_to_f16x8(ub[0], ub[1]), a11 = f8x8_to_f16x8(ub[2], ub[3]);
-              const f16x8 q0 = __builtin_bit_cast(f16x8, st[2 * kk]);
-              const f16x8 q1 = __builtin_bit_cast(f16x8, st[2 * kk + 1]);
-              s0a = E::mfma(a00, q0, s0a);
-              s1a = E::mfma(a10, q0, s1a);
-              s0b = E::mfma(a01, q1, s0b);
-              s1b = E::mfma(a11, q1, s1b);
+            const bf16x8 qv = __builtin_bit_cast(bf16x8, st[kk]);
+            if constexpr (kk & 1) {
+              s0b = E::mfma(ra[kk % P::kSRing], qv, s0b);
+              s1b = E::mfma(rb[kk % P::kSRing], qv, s1b);
             } else {
-              const bf16x8 qv = __builtin_bit_cast(bf16x8, st[kk]);
-              if constexpr (kk & 1) {
-                s0b = E::mfma(ra[kk % P::kSRing], qv, s0b);
-                s1b = E::mfma(rb[kk % P::kSRing], qv, s1b);
-              } else {
-                s0a = E::mfma(ra[kk % P::kSRing], qv, s0a);
-                s1a = E::mfma(rb[kk % P::kSRing], qv, s1a);
-              }
+              s0a = E::mfma(ra[kk % P::kSRing], qv, s0a);
+              s1a = E::mfma(rb[kk % P::kSRing], qv, s1a);
             }
-            // copies n in [n0, n1) go out after this read
-            constexpr int n0 = kk < P::kSSpread ? kk * P::kPerWave / P::kSSpread : P::kPerWave;
-            constexpr int n1 = kk < P::kSSpread ? (kk + 1) * P::kPerWave / P::kSSpread : P::kPerWave;
-            static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
           });
           const f32x4 sv0 = s0a + s0b, sv1 = s1a + s1b;
 
           // Online softmax of head 16grp + l16 over this lane's 8 tokens
-          // (4q4 + i and 16 + 4q4 + i), exp2 domain.
+          // (4q4 + i and 16 + 4q4 + i), exp2 domain: x_i = c s_i with
+          // c = |scale| log2(e) > 0 (the query carries the scale's sign), so
+          // the largest score gives the largest x, each probability is
+          // exp2(fma(s_i, c, -m)), and a masked row's -inf score gives p = 0.
+          float sc[8] = {sv0[0], sv0[1], sv0[2], sv0[3], sv1[0], sv1[1], sv1[2], sv1[3]};
           const unsigned vm = ti.rows();
-          float x[8], sig[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[i] = sv0[i] * a.scale_log2;
-            x[4 + i] = sv1[i] * a.scale_log2;
-          }
-          if constexpr (FP8) {
-            wait_lgkm<0>(sc0, sc1);  // (arrived before the last fragments)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              sig[i] = __int_as_float(sc0[i]);
-              sig[4 + i] = __int_as_float(sc1[i]);
-              x[i] *= sig[i];
-              x[4 + i] *= sig[4 + i];
-            }
-          }
-          if (vm != 0xffffffffu) {  // a tile with rows past the end (wave-uniform)
+          if (vm != 0xffffffffu) {  // rows past the end (wave-uniform)
             const unsigned lo = vm >> (4 * q4), hi = vm >> (16 + 4 * q4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              x[i] = (lo >> i) & 1u ? x[i] : -INFINITY;
-              x[4 + i] = (hi >> i) & 1u ? x[4 + i] : -INFINITY;
+              sc[i] = (lo >> i) & 1u ? sc[i] : -INFINITY;
+              sc[4 + i] = (hi >> i) & 1u ? sc[4 + i] : -INFINITY;
             }
           }
-          float hmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-          hmax = max_xor32(max_xor16(hmax));
+          const float hmax = vmax_xor32(vmax_xor16(vmax8(sc))) * qsl;
           // The reference only rises when the tile's max exceeds it by more
           // than kRaise, so probabilities stay <= 2^kRaise and rescales are rare.
           const bool raise = hmax > m_ref + P::kRaise;
           const float alpha = raise ? fast_exp2(m_ref - hmax) : 1.f;  // 0 when m_ref = -inf
           m_ref = raise ? hmax : m_ref;
-          const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+          const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
           float pr[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(x[i] - m_use);
+          for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(fmaf(sc[i], qsl, nm));
           l_run = l_run * alpha +
                   (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
-          if constexpr (FP8) {
-            // the value waves weight each token's codes by p * scale
-#pragma unroll
-            for (int i = 0; i < 8; ++i) pr[i] *= sig[i];
-          }
           const i32x4 pk = {static_cast<int>(E::pack2(pr[0], pr[1])),
                             static_cast<int>(E::pack2(pr[2], pr[3])),
                             static_cast<int>(E::pack2(pr[4], pr[5])),
                             static_cast<int>(E::pack2(pr[6], pr[7]))};
-          if constexpr (!FP8) l_rnd = add_bf16x8(pk, l_rnd * alpha);
+          l_rnd = add_bf16x8(pk, l_rnd * alpha);
           lds_store_b128(aux_addr + P::kPOff + (ks & 1) * P::kPBufB + (grp * 64 + lane) * 16, pk);
           const bool any = __ballot(raise) != 0ull;
           if (lane == 0) lds_store_b8(flags_addr + (ks & 1) * 4 + grp, any ? 1 : 0);
           if (any && q4 == 0)
             lds_store_b32(aux_addr + P::kAlphaOff + (((ks & 1) * 16 + l16) * 4 + grp) * 4, alpha);
           if (ti.last()) {
-            // Segment done: its head sums for the value waves (bf16: of the
-            // rounded probabilities), and its LSE.
+            // Segment done: its head sums for the value waves (of the rounded
+            // probabilities), and its LSE.
             const float l_h = sum_xor32(sum_xor16(l_run));
-            const float l_o = FP8 ? l_h : sum_xor32(sum_xor16(l_rnd));
+            const float l_o = sum_xor32(sum_xor16(l_rnd));
             if (q4 == 0) {
               lds_store_b32(aux_addr + P::kFinOff + ((nfin & 1) * 64 + 16 * grp + l16) * 4, l_o);
               const size_t slot = static_cast<size_t>(piece_b(ti.piece())) + g;

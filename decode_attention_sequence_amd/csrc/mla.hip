@@ -273,13 +273,15 @@ struct Elt<true> {
 //  * query: each head's query is multiplied by 2^-e with e the exponent of
 //    its largest magnitude (so |q| < 1, and components down to 2^-14 of the
 //    largest keep full precision); the score scale takes 2^e back in fp32;
-//  * probability x scale: a tile's largest token scale is below 2^E (E its
-//    exponent), so p * sigma <= 2^(x_max + E - m) for the tile's largest score
-//    x_max against reference m. Raising the reference on x_max + E rather than
-//    on x_max keeps every fp16 weight p * sigma below 2^kRaise, whatever sigma
-//    is; the fp32 probabilities p (and their sum) take the shift 2^-E, which
-//    stays far inside fp32 for scales in [2^-64, 2^64] (E is clamped at -64 so
-//    that smaller scales cannot push the sum towards overflow).
+//  * probability x scale: for any set of tokens whose largest score is x_max
+//    and whose largest scale is below 2^E (E its exponent), every
+//    p * sigma <= 2^(x_max + E - m) against reference m. The reference rises
+//    on the largest such bound over the lanes (or halves) holding a head's
+//    tokens rather than on the largest score, which keeps every fp16 weight
+//    p * sigma below 2^kRaise whatever sigma is; the fp32 probabilities p (and
+//    their sum) take the shift 2^-E, which stays far inside fp32 for scales in
+//    [2^-64, 2^64] (E is clamped at -64 so that smaller scales cannot push the
+//    sum towards overflow).
 __device__ __forceinline__ int max_exponent_head(float amax) {
   return __builtin_amdgcn_frexp_expf(amax);  // amax < 2^e (0 for amax = 0)
 }
@@ -902,16 +904,16 @@ struct PP {
   static constexpr int kStages = FP8 ? 7 : 4;                // ring stages
   static constexpr int kAhead = kStages - (kPipe ? 3 : 2);   // tiles copied ahead of the scores
   static constexpr int kMT = 8;                              // 16-column M tiles per value wave
-  // Waves that issue the tile copies: bf16, the four value waves (the score
-  // waves' instruction stream is the longer one); fp8, all eight.
-  static constexpr int kCopyWaves = FP8 ? 8 : 4;
+  // Waves that issue the tile copies: the four value waves (the score waves'
+  // instruction stream is the longer one).
+  static constexpr int kCopyWaves = 4;
   static constexpr int kPerWave = (kInst + kCopyWaves - 1) / kCopyWaves;  // copy rounds per tile
   // Copy groups cw < kCodeHi issue kPerWave code copies per tile, the others
   // one fewer (bf16). fp8: group kCodeHi copies the token scales instead and
   // the remaining groups a filler, so every wave issues kPerWave copies.
   static constexpr int kCodeHi = kInst % kCopyWaves ? kInst % kCopyWaves : kCopyWaves;
-  static constexpr int kHiWaves = FP8 ? 8 : kCodeHi;         // groups with kPerWave operations
-  static constexpr int kSmAt = 2;                            // fp8: softmax after this score read
+  static constexpr int kHiWaves = FP8 ? kCopyWaves : kCodeHi;  // groups with kPerWave operations
+  static constexpr int kSmAt = 8;                            // fp8: softmax after this score read (the last)
   static constexpr int kSteps = FP8 ? kKSteps / 2 : kKSteps;    // score fragment reads per M tile
   static constexpr int kSDist = 3;                           // score reads in flight (per M tile)
   static constexpr int kSRing = kSDist + 2;
@@ -935,11 +937,17 @@ struct PP {
   static constexpr int kPOff = 0;                            // [2] tiles
   static constexpr int kAlphaOff = kPOff + 2 * kPBufB;       // [2][16 lanes][4 groups] floats
   static constexpr int kFlagOff = kAlphaOff + 2 * 64 * 4;    // [2][4] bytes
-  static constexpr int kFinOff = kFlagOff + 16;              // [2][64] head sums
-  static constexpr int kPieceOff = kFinOff + 2 * 64 * 4;     // [kMaxPieces] x 2 int4
+  // Finished segments' head sums: bf16 [2][64]; fp8 [2][2 token halves][64]
+  // partial sums, then [2][64] reference maxima.
+  static constexpr int kFinOff = kFlagOff + 16;
+  static constexpr int kFinMOff = kFinOff + (FP8 ? 2 * 2 * 64 * 4 : 0);
+  static constexpr int kFinB = FP8 ? 3 * 2 * 64 * 4 : 2 * 64 * 4;
+  static constexpr int kPieceOff = kFinOff + kFinB;          // [kMaxPieces] x 2 int4
   static constexpr int kTileOff = kPieceOff + kMaxPieces * 32;  // [kMaxTiles] int2
   static constexpr int kMiscOff = kTileOff + kMaxTiles * 8;     // tiles, window end
-  static constexpr int kAuxB = kMiscOff + 16;
+  // fp8: each token half's bounds of its heads, [2 tiles][2 head pairs][2 halves][16][2]
+  static constexpr int kXbOff = kMiscOff + 16;
+  static constexpr int kAuxB = kXbOff + (FP8 ? 2 * 2 * 2 * 16 * 2 * 4 : 0);
   static_assert(kRingB + kAuxB <= 160 * 1024, "LDS budget");
 };
 // Tile table entry: x = block id (-1: unusable, the tile's rows read zeros),
@@ -951,6 +959,10 @@ struct PP {
 
 __device__ __forceinline__ void lds_store_b32(uint32_t addr, float v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void lds_store_b64(uint32_t addr, i32x2 v) {
+  asm volatile("ds_write_b64 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
 }
 __device__ __forceinline__ void lds_store_b128(uint32_t addr, i32x4 v) {
   asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
@@ -1037,10 +1049,10 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   const int bs = a.map.bs;
   const int D = a.map.D;
 
-  // Copies: copy group cw issues slots cw + 8n of a tile. The value waves take
-  // the groups with the extra copy (their MFMA loop has more room for them).
-  const int cw = FP8 ? (w + 4) & 7 : w - 4;
-  const bool copier = FP8 || !scorer;
+  // Copies: value wave 4 + cw issues slots cw + 4n of a tile (the score
+  // waves issue none: theirs is the longer instruction stream).
+  const int cw = w - 4;  // copy group of a value wave
+  const bool copier = !scorer;
   // Every wave issues the same copies for every step, also past the end of a
   // window (fillers that read nothing), so each wait for a tile's copies is a
   // constant count.
@@ -1072,8 +1084,8 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   }
   auto wait_tiles = [&]() {
     if (!copier) return;
-    if (hi_wave) wait_tiles_after_n<P::kPerWave, 1>(kAhead - 1);
-    else wait_tiles_after_n<P::kPerWave - 1, 1>(kAhead - 1);
+    if (hi_wave) wait_tiles_after_n<P::kPerWave, kAhead - 1>(kAhead - 1);
+    else wait_tiles_after_n<P::kPerWave - 1, kAhead - 1>(kAhead - 1);
   };
 
   // Score waves: A fragments of M tile 0 (row l16) and 1 (row 16 + l16).
@@ -1206,44 +1218,58 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   // of the other as never live at the same time.
   auto run = [&](auto role) {
     constexpr bool kScorer = decltype(role)::value;
-    // Score waves: the 18 query fragments of head head0 + 16grp + l16 of
-    // sequence qb (B operand of S^T, K step kk; fp16 for an fp8 cache). Value
-    // waves: O^T accumulators, M tile mt and head tile nt at 4mt + nt.
-    constexpr int kSt = kScorer ? kKSteps : 4 * P::kMT;
+    // Score waves: the query fragments (B operand of S^T, K step kk) -- bf16:
+    // 18 of head head0 + 16grp + l16; fp8 (fp16 fragments): 18 of each of
+    // heads head0 + 32hp + 16nt + l16, nt = 0, 1, at 18nt + kk. Value waves:
+    // O^T accumulators, M tile mt and head tile nt at 4mt + nt.
+    constexpr int kQTiles = FP8 ? 2 : 1;
+    constexpr int kSt = kScorer ? kQTiles * kKSteps : 4 * P::kMT;
     f32x4 st[kSt];
 #pragma unroll
     for (int i = 0; i < kSt; ++i) st[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     int qb = -1;
-    float qsl = a.scale_log2;  // fp8: score scale of the loaded query (log2 units)
+    float qsl[kQTiles];  // score scale (log2 units) of each loaded head
+#pragma unroll
+    for (int nt = 0; nt < kQTiles; ++nt) qsl[nt] = a.scale_log2;
+    const int hp = grp >> 1, th = grp & 1;  // fp8 score waves: head pair, token half
     auto load_q = [&](int b) {
+      if constexpr (kScorer) {
       // K step kk covers query columns 32kk + 8q4 .. +7 (bf16), or
       // 64(kk / 2) + 16q4 + 8(kk % 2) .. +7 (fp8, the chunk order above).
-      const uint16_t* qrow =
-          a.q + (static_cast<size_t>(b) * a.Hq + head0 + 16 * grp + l16) * kQK + (FP8 ? 16 : 8) * q4;
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) {
-        const int col = FP8 ? 64 * (kk >> 1) + 8 * (kk & 1) : 32 * kk;
-        st[kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + col));
+      for (int nt = 0; nt < kQTiles; ++nt) {
+        const int head = FP8 ? head0 + 32 * hp + 16 * nt + l16 : head0 + 16 * grp + l16;
+        const uint16_t* qrow =
+            a.q + (static_cast<size_t>(b) * a.Hq + head) * kQK + (FP8 ? 16 : 8) * q4;
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk) {
+          const int col = FP8 ? 64 * (kk >> 1) + 8 * (kk & 1) : 32 * kk;
+          st[nt * kKSteps + kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + col));
+        }
       }
       // Consume the loads here, in order: the compiler then waits for exactly
       // these loads (and what was issued before them), instead of placing a
       // wait for every outstanding copy in front of each later use.
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) asm volatile("" : "+v"(st[kk]));
+      for (int i = 0; i < kSt; ++i) asm volatile("" : "+v"(st[i]));
       if constexpr (FP8) {
-        // The head's largest magnitude over the four lanes that hold it.
-        float qm = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < kKSteps; ++kk) {
-          const bf16x8 v = __builtin_bit_cast(bf16x8, st[kk]);
+        for (int nt = 0; nt < kQTiles; ++nt) {
+          // The head's largest magnitude over the four lanes that hold it.
+          float qm = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) qm = fmaxf(qm, fabsf(static_cast<float>(v[i])));
+          for (int kk = 0; kk < kKSteps; ++kk) {
+            const bf16x8 v = __builtin_bit_cast(bf16x8, st[nt * kKSteps + kk]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qm = fmaxf(qm, fabsf(static_cast<float>(v[i])));
+          }
+          const int qe = max_exponent_head(max_xor32(max_xor16(qm)));
+#pragma unroll
+          for (int kk = 0; kk < kKSteps; ++kk)
+            st[nt * kKSteps + kk] = __builtin_bit_cast(
+                f32x4, E::from_bf16_pow2(__builtin_bit_cast(bf16x8, st[nt * kKSteps + kk]), qe));
+          qsl[nt] = __builtin_amdgcn_ldexpf(a.scale_log2, qe);
         }
-        const int qe = max_exponent_head(max_xor32(max_xor16(qm)));
-#pragma unroll
-        for (int kk = 0; kk < kKSteps; ++kk)
-          st[kk] = __builtin_bit_cast(f32x4, E::from_bf16_pow2(__builtin_bit_cast(bf16x8, st[kk]), qe));
-        qsl = __builtin_amdgcn_ldexpf(a.scale_log2, qe);
       } else {
         // The scale's sign goes into the query (an exact sign flip), so the
         // scores are multiplied by c = |scale| log2(e). A zero scale is taken
@@ -1254,12 +1280,15 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           for (int kk = 0; kk < kKSteps; ++kk)
             st[kk] = __builtin_bit_cast(f32x4, __builtin_bit_cast(i32x4, st[kk]) ^ static_cast<int>(0x80008000u));
         }
-        qsl = fmaxf(fabsf(a.scale_log2), 0x1p-100f);
+        qsl[0] = fmaxf(fabsf(a.scale_log2), 0x1p-100f);
       }
       qb = b;
+      }
     };
     float m_ref = -INFINITY;  // score waves: reference max (log2 units) of head 16grp + l16
     float l_run = 0.f;        // score waves: this lane's probability sum for that head
+    float m2[2] = {-INFINITY, -INFINITY};  // fp8: the same for heads 32hp + 16nt + l16
+    float l2[2] = {0.f, 0.f};
     float l_rnd = 0.f;        // bf16: the same sum over the probabilities as rounded for P^T
     int nfin = 0;             // segments finished so far (parity selects the fin buffer)
 
@@ -1378,93 +1407,85 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
 
       if constexpr (P::kPipe) {
        if constexpr (kScorer) {
-        i32x2 e_cur = {0, 0}, e_iss = {0, 0};
-        if (T > 0) {
-          entry_read(e_cur, 0);
-          entry_read(e_iss, min(kAhead, T - 1));
-        }
+        // fp8 score waves: wave grp = 2hp + th takes the 32 heads of head pair
+        // hp over the 16 tokens of token half th (rows 16th + l16 of the A
+        // operand; lane results are tokens 16th + 4q4 + i of heads 32hp + 16nt
+        // + l16), so each converted code feeds two MFMAs. A head's two token
+        // halves lie in the waves 2hp and 2hp + 1: at the end of step ks each
+        // writes its bounds of tile ks to LDS, and in step ks + 1 each reads
+        // the other's and runs the softmax of tile ks with the common maximum
+        // (both compute the same reference from the same two values).
+        i32x2 e_cur = {0, 0};
+        if (T > 0) entry_read(e_cur, 0);
         // Tile ks - 1, whose softmax runs in step ks: its table entry, its
-        // scores and its token scales (rows 4q4 + i and 16 + 4q4 + i).
+        // x = s sigma c (x[4nt + i]: head nt, token 16th + 4q4 + i), its token
+        // scales and this half's bound of each head.
         TileInfo tip{-1, 0};
-        f32x4 svp0 = {0.f, 0.f, 0.f, 0.f}, svp1 = svp0;
-        i32x4 scp0 = {0, 0, 0, 0}, scp1 = scp0;
-        float qslp = qsl;  // score scale of tile ks - 1's query
+        float xp[8], sgp[4], bop[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xp[i] = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sgp[i] = 0.f;
+        bop[0] = bop[1] = -INFINITY;
+        const uint32_t a_row = th ? a1e : a0e;
+        const uint32_t xb_addr = aux_addr + P::kXbOff + (hp * 2 + th) * 128 + l16 * 8;
+        const uint32_t xb_other = aux_addr + P::kXbOff + (hp * 2 + (th ^ 1)) * 128 + l16 * 8;
         for (int ks = 0; ks <= T; ++ks) {
           step_begin(ks);
           const bool has_s = ks < T;   // step ks scores tile ks ...
           const bool has_sm = ks > 0;  // ... and runs the softmax of tile ks - 1
-          TileInfo ti{-1, 0}, tiss{-1, 0};
+          TileInfo ti{-1, 0};
           if (has_s) {
             ti = entry_take(e_cur);
-            tiss = entry_take(e_iss);
             entry_read(e_cur, min(ks + 1, T - 1));
-            entry_read(e_iss, min(ks + 1 + kAhead, T - 1));
             if (ti.first()) {
               // A new sequence needs its query. (Loaded here, in the iteration
-              // that uses it, the compiler's waits for it are exact and do not
-              // drain the copies in flight.)
+              // that uses it, the compiler's waits for it are exact.)
               const int b = piece_b(ti.piece());
               if (b != qb) load_q(b);
             }
           }
           if (has_sm && tip.first()) {
-            m_ref = -INFINITY;
-            l_run = 0.f;
+            m2[0] = m2[1] = -INFINITY;
+            l2[0] = l2[1] = 0.f;
           }
           // (In the window's last step there is no tile ks: the score loop then
-          // reads a stale stage and its results are dropped; the copies are
-          // fillers.)
-          const Src nsrc = tile_src(tiss, ks + kAhead < T);
+          // reads a stale stage and its results are dropped.)
           const uint32_t tile = ring_addr + (ks % kStages) * P::kStageB;
-          i32x4 sc0, sc1;
-          lds_b128<0>(sc0, tile + P::kScaleOff + 16 * q4);
-          lds_b128<64>(sc1, tile + P::kScaleOff + 16 * q4);
-          i32x4 ra[P::kSRing], rb[P::kSRing];
+          i32x4 scr;  // scales of this lane's tokens of tile ks
+          lds_b128<0>(scr, tile + P::kScaleOff + 64 * th + 16 * q4);
+          i32x2 xo;   // the other half's bounds of tile ks - 1
+          lds_b64<0>(xo, xb_other + ((ks - 1) & 1) * 512);
+          i32x4 ra[P::kSRing];
           auto s_issue = [&](auto kc) {
             constexpr int kk = decltype(kc)::value;
-            lds_b128<64 * kk>(ra[kk % P::kSRing], tile + a0e);
-            lds_b128<64 * kk>(rb[kk % P::kSRing], tile + a1e);
+            lds_b128<64 * kk>(ra[kk % P::kSRing], tile + a_row);
           };
           static_for<0, P::kSDist>(s_issue);
 
-          // Online softmax of tile ks - 1 for head 16grp + l16 over this lane's
-          // 8 tokens, exp2 domain. Plain arithmetic placed inside the score
-          // loop, so its latency overlaps the MFMAs; its stores follow the loop.
-          i32x4 pk = {0, 0, 0, 0};
-          float alpha = 1.f, m_new = m_ref, l_new = l_run;
+          // Online softmax of tile ks - 1 for heads 32hp + 16nt + l16 over this
+          // lane's 4 tokens, exp2 domain, against the larger of the two halves'
+          // bounds (log2 bounds of p * sigma against reference 0).
+          i32x2 pk[2] = {{0, 0}, {0, 0}};
+          float alpha[2] = {1.f, 1.f}, m_new[2] = {m2[0], m2[1]}, l_new[2] = {l2[0], l2[1]};
           bool raise = false;
           auto softmax_prev = [&]() {
-            const unsigned vm = tip.rows();
-            const unsigned lo = vm >> (4 * q4), hi = vm >> (16 + 4 * q4);
-            float x[8], sig[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const bool v0 = (lo >> i) & 1u, v1 = (hi >> i) & 1u;
-              sig[i] = v0 ? __int_as_float(scp0[i]) : 0.f;
-              sig[4 + i] = v1 ? __int_as_float(scp1[i]) : 0.f;
-              x[i] = v0 ? svp0[i] * sig[i] * qslp : -INFINITY;
-              x[4 + i] = v1 ? svp1[i] * sig[4 + i] * qslp : -INFINITY;
+            for (int nt = 0; nt < 2; ++nt) {
+              const float bnd = vmax(bop[nt], __int_as_float(xo[nt]));
+              const bool up = bnd > m2[nt] + P::kRaise;
+              raise |= up;
+              alpha[nt] = up ? fast_exp2(m2[nt] - bnd) : 1.f;  // 0 when m = -inf
+              m_new[nt] = up ? bnd : m2[nt];
+              const float nm = m_new[nt] == -INFINITY ? 0.f : -m_new[nt];
+              float pr[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(xp[4 * nt + i] + nm);
+              l_new[nt] = l2[nt] * alpha[nt] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+              // the value waves weight each token's codes by p * scale
+              pk[nt] = i32x2{static_cast<int>(E::pack2(pr[0] * sgp[0], pr[1] * sgp[1])),
+                             static_cast<int>(E::pack2(pr[2] * sgp[2], pr[3] * sgp[3]))};
             }
-            float hmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                               fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-            float smax = fmaxf(fmaxf(fmaxf(fabsf(sig[0]), fabsf(sig[1])), fmaxf(fabsf(sig[2]), fabsf(sig[3]))),
-                               fmaxf(fmaxf(fabsf(sig[4]), fabsf(sig[5])), fmaxf(fabsf(sig[6]), fabsf(sig[7]))));
-            // log2 bound of this tile's p * sigma against reference 0
-            hmax = max_xor32(max_xor16(hmax)) + scale_exponent(max_xor32(max_xor16(smax)));
-            raise = hmax > m_ref + P::kRaise;
-            alpha = raise ? fast_exp2(m_ref - hmax) : 1.f;  // 0 when m_ref = -inf
-            m_new = raise ? hmax : m_ref;
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            float pr[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(x[i] - m_use);
-            l_new = l_run * alpha +
-                    (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
-            // the value waves weight each token's codes by p * scale
-            pk = i32x4{static_cast<int>(E::pack2(pr[0] * sig[0], pr[1] * sig[1])),
-                       static_cast<int>(E::pack2(pr[2] * sig[2], pr[3] * sig[3])),
-                       static_cast<int>(E::pack2(pr[4] * sig[4], pr[5] * sig[5])),
-                       static_cast<int>(E::pack2(pr[6] * sig[6], pr[7] * sig[7]))};
           };
 
           f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
@@ -1472,55 +1493,94 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             constexpr int kk = decltype(kc)::value;
             if constexpr (kk + P::kSDist < P::kSteps) s_issue(IC<kk + P::kSDist>{});
             constexpr int ahead = kk + P::kSDist < P::kSteps ? P::kSDist : P::kSteps - 1 - kk;
-            wait_lgkm<2 * ahead>(ra[kk % P::kSRing], rb[kk % P::kSRing]);
-            // read kk: K steps 2kk (codes 0-7) and 2kk + 1 (codes 8-15)
-            const i32x4 ua = ra[kk % P::kSRing], ub = rb[kk % P::kSRing];
-            const i32x4 a00 = f8x8_to_f16x8(ua[0], ua[1]), a01 = f8x8_to_f16x8(ua[2], ua[3]);
-            const i32x4 a10 = f8x8_to_f16x8(ub[0], ub[1]), a11 = f8x8_to_f16x8(ub[2], ub[3]);
-            const f16x8 q0 = __builtin_bit_cast(f16x8, st[2 * kk]);
-            const f16x8 q1 = __builtin_bit_cast(f16x8, st[2 * kk + 1]);
-            s0a = E::mfma(a00, q0, s0a);
-            s1a = E::mfma(a10, q0, s1a);
-            s0b = E::mfma(a01, q1, s0b);
-            s1b = E::mfma(a11, q1, s1b);
+            // (LDS reads complete in order: once read kk is in, so are the
+            // scales and the other half's bounds issued before it.)
+            if constexpr (kk == 0) wait_lgkm<ahead>(ra[0], xo);
+            else wait_lgkm<ahead>(ra[kk % P::kSRing]);
+            // read kk: K steps 2kk (codes 0-7) and 2kk + 1 (codes 8-15) of row
+            // 16th + l16, for both heads of the lane
+            const i32x4 ua = ra[kk % P::kSRing];
+            const i32x4 a0 = f8x8_to_f16x8(ua[0], ua[1]), a1 = f8x8_to_f16x8(ua[2], ua[3]);
+            s0a = E::mfma(a0, __builtin_bit_cast(f16x8, st[2 * kk]), s0a);
+            s1a = E::mfma(a0, __builtin_bit_cast(f16x8, st[kKSteps + 2 * kk]), s1a);
+            s0b = E::mfma(a1, __builtin_bit_cast(f16x8, st[2 * kk + 1]), s0b);
+            s1b = E::mfma(a1, __builtin_bit_cast(f16x8, st[kKSteps + 2 * kk + 1]), s1b);
             if constexpr (kk == P::kSmAt) softmax_prev();
-            // copies n in [n0, n1) go out after this read
-            constexpr int n0 = kk < P::kSSpread ? kk * P::kPerWave / P::kSSpread : P::kPerWave;
-            constexpr int n1 = kk < P::kSSpread ? (kk + 1) * P::kPerWave / P::kSSpread : P::kPerWave;
-            static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
           });
-          const f32x4 sv0 = s0a + s0b, sv1 = s1a + s1b;
+          const f32x4 sv[2] = {s0a + s0b, s1a + s1b};
 
-          // Results of tile ks - 1. (A window's first step has none: its stores
-          // land in buffers that tile 1 rewrites before any value wave reads them.)
+          // Results of tile ks - 1. (A window's first step has none.)
           const int pp = (ks - 1) & 1;
-          lds_store_b128(aux_addr + P::kPOff + pp * P::kPBufB + (grp * 64 + lane) * 16, pk);
+          if (has_sm) {
+            const uint32_t pdst = aux_addr + P::kPOff + pp * P::kPBufB + lane * 16 + 8 * th;
+            lds_store_b64<0>(pdst + (2 * hp) * 1024, pk[0]);
+            lds_store_b64<0>(pdst + (2 * hp + 1) * 1024, pk[1]);
+          }
           const bool any = has_sm && __ballot(raise) != 0ull;
           if (lane == 0) lds_store_b8(flags_addr + pp * 4 + grp, any ? 1 : 0);
-          if (any && q4 == 0)
-            lds_store_b32(aux_addr + P::kAlphaOff + ((pp * 16 + l16) * 4 + grp) * 4, alpha);
+          if (any && th == 0 && q4 == 0)
+            lds_store_b64<0>(aux_addr + P::kAlphaOff + ((pp * 16 + l16) * 4 + 2 * hp) * 4,
+                             i32x2{__float_as_int(alpha[0]), __float_as_int(alpha[1])});
           if (has_sm) {
-            m_ref = m_new;
-            l_run = l_new;
+            m2[0] = m_new[0];
+            m2[1] = m_new[1];
+            l2[0] = l_new[0];
+            l2[1] = l_new[1];
           }
           if (has_sm && tip.last()) {
-            // Segment done: its head sums for the value waves, and its LSE.
-            const float l_h = sum_xor32(sum_xor16(l_run));
+            // Segment done: this half's head sums and (half 0) the reference
+            // maxima, for the value waves' normalisation and LSE.
+            const float lh0 = sum_xor32(sum_xor16(l2[0])), lh1 = sum_xor32(sum_xor16(l2[1]));
             if (q4 == 0) {
-              lds_store_b32(aux_addr + P::kFinOff + ((nfin & 1) * 64 + 16 * grp + l16) * 4, l_h);
-              const size_t slot = static_cast<size_t>(piece_b(tip.piece())) + g;
-              a.ws_lse[slot * a.Hq + head0 + 16 * grp + l16] =
-                  l_h > 0.f ? (m_ref + fast_log2(l_h)) * kLn2 : -INFINITY;
+              const uint32_t fl = aux_addr + P::kFinOff + (((nfin & 1) * 2 + th) * 64 + 32 * hp + l16) * 4;
+              lds_store_b32(fl, lh0);
+              lds_store_b32(fl + 64, lh1);
+              if (th == 0) {
+                const uint32_t fm = aux_addr + P::kFinMOff + ((nfin & 1) * 64 + 32 * hp + l16) * 4;
+                lds_store_b32(fm, m2[0]);
+                lds_store_b32(fm + 64, m2[1]);
+              }
             }
             ++nfin;
           }
-          wait_lgkm<0>(sc0, sc1);
+
+          // Tile ks: x, and this half's bound of each head (the lanes' largest
+          // x plus the exponent of their largest scale, over the four lanes
+          // holding the head), written for the other half.
+          wait_lgkm<0>(scr);
+          float sg[4], xn[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sg[i] = __int_as_float(scr[i]);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xn[4 * nt + i] = sv[nt][i] * sg[i] * qsl[nt];
+          const unsigned vm = ti.rows();
+          if (vm != 0xffffffffu) {  // rows past the end (wave-uniform)
+            const unsigned rb = vm >> (16 * th + 4 * q4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool v = (rb >> i) & 1u;
+              sg[i] = v ? sg[i] : 0.f;
+              xn[i] = v ? xn[i] : -INFINITY;
+              xn[4 + i] = v ? xn[4 + i] : -INFINITY;
+            }
+          }
+          const float e = scale_exponent(vmax(vmax(sg[0], sg[1]), vmax(sg[2], sg[3])));
+          float bn[2];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            bn[nt] = vmax_xor32(vmax_xor16(vmax(vmax(xn[4 * nt], xn[4 * nt + 1]),
+                                                vmax(xn[4 * nt + 2], xn[4 * nt + 3])) + e));
+          if (has_s && q4 == 0)
+            lds_store_b64<0>(xb_addr + (ks & 1) * 512, i32x2{__float_as_int(bn[0]), __float_as_int(bn[1])});
           tip = ti;
-          qslp = qsl;
-          svp0 = sv0;
-          svp1 = sv1;
-          scp0 = sc0;
-          scp1 = sc1;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xp[i] = xn[i];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sgp[i] = sg[i];
+          bop[0] = bn[0];
+          bop[1] = bn[1];
         }
         step_begin(T + 1);  // the value waves' last step
        } else {
@@ -1568,14 +1628,16 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           wait_lgkm<4 + P::kMT>(fl);
           const int fb = wave_uniform(fl);
           if (fb != 0) {
-            // Rescale factors of heads whose reference max rose in tile kv.
+            // Rescale factors of heads whose reference max rose in tile kv
+            // (vote byte 2hp, the pair's first half, covers head tiles 2hp and
+            // 2hp + 1; a head that did not rise has factor 1).
             i32x4 al;
             lds_b128<0>(al, aux_addr + P::kAlphaOff + ((kv & 1) * 16 + l16) * 16);
             wait_lgkm<0>(al);
             const f32x4 alv = __builtin_bit_cast(f32x4, al);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
-              if ((fb >> (8 * nt)) & 0xff)
+              if ((fb >> (8 * (nt & ~1))) & 0xff)
 #pragma unroll
                 for (int mt = 0; mt < P::kMT; ++mt) st[4 * mt + nt] *= alv[nt];
           }
@@ -1592,29 +1654,36 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             static_for<n0, n1>([&](auto nc) { copy_one(nc, nsrc, ks + kAhead); });
           });
           if (ti.last()) {
-            // Segment done: normalise by the score waves' head sums and store
-            // (O, slot s + g); the accumulators restart at zero.
+            // Segment done: normalise by the head sums (the two token halves'
+            // partial sums) and store (O, slot b + g); value wave 0 also stores
+            // the LSE from the reference maxima. The accumulators restart at 0.
             const size_t slot = static_cast<size_t>(piece_b(ti.piece())) + g;
-            // fin[16nt + l16] for nt = 0..3
-            const uint32_t fa = aux_addr + P::kFinOff + ((nfin & 1) * 64 + l16) * 4;
-            int l0, l1, l2, l3;
-            lds_b32<0>(l0, fa);
-            lds_b32<64>(l1, fa);
-            lds_b32<128>(l2, fa);
-            lds_b32<192>(l3, fa);
-            wait_lgkm<0>(l0, l1);
-            wait_lgkm<0>(l2, l3);
-            const float lt[4] = {__int_as_float(l0), __int_as_float(l1), __int_as_float(l2),
-                                 __int_as_float(l3)};
+            // head 16nt + l16: halves at fin[(par * 2 + half) * 64 + head], maximum at finm[par * 64 + head]
+            const uint32_t fa = aux_addr + P::kFinOff + ((nfin & 1) * 128 + l16) * 4;
+            const uint32_t fm = aux_addr + P::kFinMOff + ((nfin & 1) * 64 + l16) * 4;
+            int h0[4], h1[4], mm[4];
+            static_for<0, 4>([&](auto nc) {
+              constexpr int nt = decltype(nc)::value;
+              lds_b32<64 * nt>(h0[nt], fa);
+              lds_b32<256 + 64 * nt>(h1[nt], fa);
+              lds_b32<64 * nt>(mm[nt], fm);
+            });
+            wait_lgkm<0>(h0[0], h1[0]);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) asm volatile("" : "+v"(h0[nt]), "+v"(h1[nt]), "+v"(mm[nt]));
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-              const float inv = lt[nt] > 0.f ? 1.f / lt[nt] : 0.f;
+              const float lt = __int_as_float(h0[nt]) + __int_as_float(h1[nt]);
+              const float inv = lt > 0.f ? 1.f / lt : 0.f;
               float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
 #pragma unroll
               for (int mt = 0; mt < P::kMT; ++mt) {
                 *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
                 st[4 * mt + nt] = f32x4{0.f, 0.f, 0.f, 0.f};
               }
+              if (grp == 0 && q4 == 0)
+                a.ws_lse[slot * a.Hq + head0 + 16 * nt + l16] =
+                    lt > 0.f ? (__int_as_float(mm[nt]) + fast_log2(lt)) * kLn2 : -INFINITY;
             }
             ++nfin;
           }
@@ -1685,7 +1754,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
               sc[4 + i] = (hi >> i) & 1u ? sc[4 + i] : -INFINITY;
             }
           }
-          const float hmax = vmax_xor32(vmax_xor16(vmax8(sc))) * qsl;
+          const float hmax = vmax_xor32(vmax_xor16(vmax8(sc))) * qsl[0];
           // The reference only rises when the tile's max exceeds it by more
           // than kRaise, so probabilities stay <= 2^kRaise and rescales are rare.
           const bool raise = hmax > m_ref + P::kRaise;
@@ -1694,7 +1763,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
           const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
           float pr[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(fmaf(sc[i], qsl, nm));
+          for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(fmaf(sc[i], qsl[0], nm));
           l_run = l_run * alpha +
                   (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
           const i32x4 pk = {static_cast<int>(E::pack2(pr[0], pr[1])),

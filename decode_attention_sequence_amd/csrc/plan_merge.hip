@@ -56,30 +56,20 @@ WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim, 
 // [start(g), start(g + 1)); a segment's overhead units come before its first
 // block.
 // Range g runs on XCD g / (G / 8) (xcd_logical_group). On MI355X the
-// odd-numbered XCDs finish the same work 2-4 % later than the even ones
-// (per-work-group finishing times on three boxes, whatever ranges they get),
-// so their ranges get a share of the cost smaller by kWOdd / kWEven.
 // Arrays the plan searches are mirrored in LDS when they fit (flat pointers
 // then address LDS), else read from the workspace.
 constexpr int kPlanLds = 6144;  // entries per mirrored array
-constexpr int kWEven = 40, kWOdd = 39;
 
-// First cost position of range g (start(G) = total cost). Below 8 cost units
-// per range the split is uniform, cc = ceil(total / G) units per range, which
-// leaves no range without cost units before the last block; above it the
-// weighted ranges all hold several units as well.
+// First cost position of range g (start(G) = total cost): an equal share of
+// the cost per range. Below 8 cost units per range the split is in whole
+// units, cc = ceil(total / G) per range, which leaves no range without cost
+// units before the last block.
 __device__ __forceinline__ int split_start(int total_c, int G, int g) {
-  if ((G & 7) || total_c < 8 * G) {
+  if (total_c < 8 * G) {
     const long long cc = max(1, (total_c + G - 1) / G);
     return static_cast<int>(min(static_cast<long long>(g) * cc, static_cast<long long>(total_c)));
   }
-  const int per = G >> 3;
-  const int x = g / per, k = g - x * per;
-  const long long w = static_cast<long long>((x + 1) >> 1) * per * kWEven +
-                      static_cast<long long>(x >> 1) * per * kWOdd +
-                      static_cast<long long>(k) * ((x & 1) ? kWOdd : kWEven);
-  const long long all = 4ll * per * (kWEven + kWOdd);
-  return static_cast<int>(static_cast<long long>(total_c) * w / all);
+  return static_cast<int>(static_cast<long long>(total_c) * g / G);
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int seg_cost, int Hq,

@@ -221,9 +221,11 @@ def copy_probe(mib: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # A step is about a millisecond: the defaults time the sustained rate (the
-    # first few calls after start-up run a few percent slower) in well under
-    # a second of GPU time.
+    # A step is about a millisecond. In a fresh process the attention kernel's
+    # launches 3 to about 20 run up to 45 % slower than later ones when
+    # launched back to back (a transient of the GPU's power management), so the
+    # defaults time 100 steps after 20 warm-up steps; `--steps 20 --warmup 5`
+    # reads about 5-8 % below this sustained rate.
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.SPECS))

@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import ctypes
 import math
+import os
 from pathlib import Path
 from typing import Optional
 
@@ -31,7 +32,10 @@ __all__ = [
     "decode_partial", "decode_partial_mtp", "lse_merge", "decode_all_shards", "status_str", "version",
 ]
 
-_LIB_PATH = Path(__file__).resolve().with_name("libdcp.so")
+# The library the binding loads: the in-tree build, or the file named by the
+# DCP_LIBRARY environment variable (e.g. a build with host-side sanitizers).
+_LIB_PATH = (Path(os.environ["DCP_LIBRARY"]).resolve() if os.environ.get("DCP_LIBRARY")
+             else Path(__file__).resolve().with_name("libdcp.so"))
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 KV_SEPARATE, KV_LATENT = 0, 1

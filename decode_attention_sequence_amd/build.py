@@ -2,7 +2,12 @@
 
 Each translation unit is compiled to an object in parallel, then linked into
 ``decode_attention_sequence_amd/libdcp.so``. Usage: ``python -m
-decode_attention_sequence_amd.build [-v]``.
+decode_attention_sequence_amd.build [-v] [--host-sanitizers]``.
+
+``--host-sanitizers`` builds a second copy, ``_build/sanitize/libdcp_host_sanitized.so``,
+whose host code runs under AddressSanitizer and UndefinedBehaviorSanitizer
+(device code unchanged). It needs the sanitizer runtime preloaded into the
+process that loads it; the CPU tests use it to drive the C ABI's argument checks.
 """
 from __future__ import annotations
 
@@ -42,8 +47,19 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, verbose: bool, extra) -> Path:
-    obj = BUILD_DIR / (Path(src).stem + ".o")
+# Host-only sanitizers: each -fsanitize= goes to the host compilation alone.
+HOST_SANITIZE_FLAGS = [
+    "-Xarch_host", "-g",
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+SANITIZED_LIB = BUILD_DIR / "sanitize" / "libdcp_host_sanitized.so"
+
+
+def _compile(src: str, verbose: bool, extra, out_dir: Path = BUILD_DIR) -> Path:
+    obj = out_dir / (Path(src).stem + ".o")
     cmd = [hipcc(), *HIP_FLAGS, *extra, "-c", str(CSRC / src), "-o", str(obj)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # The host pass warns that it does not know the packed-fp32 target feature.
@@ -56,20 +72,46 @@ def _compile(src: str, verbose: bool, extra) -> Path:
     return obj
 
 
-def build(verbose: bool = False, extra_flags=()) -> Path:
-    BUILD_DIR.mkdir(exist_ok=True)
-    with ThreadPoolExecutor(min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, list(extra_flags)), SOURCES))
-    tmp = LIB.with_suffix(".so.tmp")
+def _link(objs, lib: Path) -> Path:
+    tmp = lib.with_suffix(".so.tmp")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, extra_flags=()) -> Path:
+    BUILD_DIR.mkdir(exist_ok=True)
+    with ThreadPoolExecutor(min(len(SOURCES), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose, list(extra_flags)), SOURCES))
+    _link(objs, LIB)
     if verbose:
         print(f"built {LIB}")
     return LIB
 
 
+def build_host_sanitized(verbose: bool = False) -> Path:
+    """The library with AddressSanitizer and UndefinedBehaviorSanitizer on its
+    host code, rebuilt when a source or header is newer than it. The sanitizer
+    symbols stay undefined in the library: load it only into a process that
+    has the runtime (libclang_rt.asan) preloaded."""
+    out = SANITIZED_LIB.parent
+    out.mkdir(parents=True, exist_ok=True)
+    inputs = [*CSRC.iterdir(), *INCLUDE.iterdir(), Path(__file__)]
+    if SANITIZED_LIB.exists() and all(p.stat().st_mtime <= SANITIZED_LIB.stat().st_mtime for p in inputs):
+        return SANITIZED_LIB
+    with ThreadPoolExecutor(min(len(SOURCES), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose, HOST_SANITIZE_FLAGS, out), SOURCES))
+    _link(objs, SANITIZED_LIB)
+    if verbose:
+        print(f"built {SANITIZED_LIB}")
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    if "--host-sanitizers" in sys.argv:
+        build_host_sanitized(verbose="-v" in sys.argv)
+    else:
+        build(verbose="-v" in sys.argv)

@@ -44,7 +44,7 @@ dcp_status_t noalloc_scratch_ptr(hipStream_t stream, void** out) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int elt_bytes(dcp_dtype_t t) { return t == DCP_F32 ? 4 : (t == DCP_BF16 ? 2 : 1); }
+int elt_bytes(int32_t t) { return t == DCP_F32 ? 4 : (t == DCP_BF16 ? 2 : 1); }
 
 bool valid_dtype(int t) { return t == DCP_F32 || t == DCP_BF16 || t == DCP_FP8_E4M3; }
 
@@ -162,7 +162,7 @@ dcp_status_t shard_partial(const dcp_attn_desc_t* d, int shard, const int32_t* q
 
 extern "C" {
 
-const char* dcp_status_str(dcp_status_t s) {
+const char* dcp_status_str(int32_t s) {
   switch (s) {
     case DCP_OK: return "ok";
     case DCP_ERR_INVALID_ARG: return "invalid argument";
@@ -187,7 +187,7 @@ size_t dcp_workspace_size(const dcp_attn_desc_t* d) {
 
 dcp_status_t dcp_block_remap_ex(const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
                                 int32_t max_blocks, int32_t block_size, int32_t num_shards,
-                                dcp_ownership_t ownership, int32_t* local_block_table,
+                                int32_t ownership, int32_t* local_block_table,
                                 int32_t* local_seq_lens, hipStream_t stream) {
   if (!block_table || !seq_lens || !local_block_table || !local_seq_lens) return DCP_ERR_INVALID_ARG;
   if (batch < 1 || max_blocks < 1 || block_size < 1 || num_shards < 1) return DCP_ERR_INVALID_ARG;
@@ -233,7 +233,7 @@ dcp_status_t dcp_block_remap_update(const int32_t* block_table, const int32_t* o
 
 dcp_status_t dcp_kv_append(const dcp_attn_desc_t* d, int32_t num_tokens, const int32_t* token_seq,
                            const int32_t* positions, const void* k_new, const void* v_new,
-                           dcp_dtype_t new_dtype, int32_t shard, const int32_t* block_table,
+                           int32_t new_dtype, int32_t shard, const int32_t* block_table,
                            void* k_cache, void* v_cache, float* kv_scale, hipStream_t stream) {
   const dcp_status_t st = check_desc(d);
   if (st != DCP_OK) return st;
@@ -250,7 +250,8 @@ dcp_status_t dcp_kv_append(const dcp_attn_desc_t* d, int32_t num_tokens, const i
     return DCP_ERR_INVALID_ARG;
   if (d->kv_dtype == DCP_FP8_E4M3 && (!kv_scale || !aligned(kv_scale, 4)))
     return DCP_ERR_INVALID_ARG;
-  if (launch_kv_append(d, num_tokens, token_seq, positions, k_new, v_new, new_dtype, shard,
+  if (launch_kv_append(d, num_tokens, token_seq, positions, k_new, v_new,
+                       static_cast<dcp_dtype_t>(new_dtype), shard,
                        block_table, k_cache, v_cache, kv_scale, stream) != hipSuccess)
     return DCP_ERR_HIP;
   return DCP_OK;
@@ -325,7 +326,7 @@ dcp_status_t dcp_decode_partial_token(const dcp_attn_desc_t* d, int32_t shard, c
 
 dcp_status_t dcp_lse_merge(const float* o_partials, const float* lse_partials,
                            int32_t num_partials, int32_t batch, int32_t num_heads, int32_t v_dim,
-                           void* out, dcp_dtype_t out_dtype, float* lse_out, hipStream_t stream) {
+                           void* out, int32_t out_dtype, float* lse_out, hipStream_t stream) {
   if (!o_partials || !lse_partials || !out) return DCP_ERR_INVALID_ARG;
   if (num_partials < 1 || batch < 1 || num_heads < 1 || v_dim < 4) return DCP_ERR_INVALID_ARG;
   if (out_dtype != DCP_F32 && out_dtype != DCP_BF16) return DCP_ERR_INVALID_ARG;
@@ -335,7 +336,7 @@ dcp_status_t dcp_lse_merge(const float* o_partials, const float* lse_partials,
   if (!aligned(o_partials, 16) || !aligned(out, out_dtype == DCP_F32 ? 16 : 8))
     return DCP_ERR_INVALID_ARG;
   if (launch_merge_partials(o_partials, lse_partials, num_partials, batch, num_heads, v_dim, out,
-                            out_dtype, lse_out, stream) != hipSuccess)
+                            static_cast<dcp_dtype_t>(out_dtype), lse_out, stream) != hipSuccess)
     return DCP_ERR_HIP;
   return DCP_OK;
 }
@@ -391,8 +392,8 @@ dcp_status_t dcp_decode_all_shards_timed(const dcp_attn_desc_t* d, const void* q
   map.tok_D = 1;
   const Causal cz{nullptr, desc_q_len(d), d->num_q_heads, 0, 1};
   return run_attention(d, q, k_cache, v_cache, kv_scale, map, d->batch * d->num_shards, cz, out,
-                       d->out_dtype, lse_out, workspace, workspace_bytes, stream, attn_begin,
-                       attn_end);
+                       static_cast<dcp_dtype_t>(d->out_dtype), lse_out, workspace, workspace_bytes,
+                       stream, attn_begin, attn_end);
 }
 
 }  // extern "C"

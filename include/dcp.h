@@ -69,7 +69,10 @@ typedef enum {
   DCP_KV_LATENT = 1
 } dcp_kv_kind_t;
 
-/* Shape and types of one decode-attention layer call. */
+/* Shape and types of one decode-attention layer call. Fields and arguments
+ * that take one of the enumerations above are int32_t holding its value, so
+ * that any value a caller stores is well defined to read (out-of-range values
+ * are rejected with DCP_ERR_INVALID_ARG). */
 typedef struct {
   uint32_t struct_size;      /* sizeof(dcp_attn_desc_t), for ABI versioning */
   int32_t batch;             /* B, sequences (one query token each) */
@@ -82,10 +85,11 @@ typedef struct {
   int32_t num_shards;        /* D >= 1 */
   int32_t max_seq_len;       /* host upper bound of any seq_len (sizes the workspace) */
   int32_t num_cache_blocks;  /* physical blocks in the cache pool (>= 0) */
-  dcp_kv_kind_t kv_kind;
-  dcp_dtype_t q_dtype;       /* DCP_F32 or DCP_BF16 */
-  dcp_dtype_t kv_dtype;      /* DCP_F32, DCP_BF16 or DCP_FP8_E4M3 (latent only) */
-  dcp_dtype_t out_dtype;     /* final output of dcp_decode_all_shards: DCP_F32 or DCP_BF16 */
+  int32_t kv_kind;           /* a dcp_kv_kind_t */
+  int32_t q_dtype;           /* a dcp_dtype_t: DCP_F32 or DCP_BF16 */
+  int32_t kv_dtype;          /* a dcp_dtype_t: DCP_F32, DCP_BF16 or DCP_FP8_E4M3 (latent only) */
+  int32_t out_dtype;         /* a dcp_dtype_t, the final output of dcp_decode_all_shards:
+                              * DCP_F32 or DCP_BF16 */
   float softmax_scale;       /* score = softmax_scale * q . k */
   int64_t kv_block_stride;   /* elements between cache blocks */
   int64_t kv_token_stride;   /* elements between tokens of a block */
@@ -150,7 +154,7 @@ typedef enum { DCP_OWN_INTERLEAVED = 0, DCP_OWN_CONTIGUOUS = 1 } dcp_ownership_t
  * dcp_block_remap is this call with DCP_OWN_INTERLEAVED. */
 dcp_status_t dcp_block_remap_ex(const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
                                 int32_t max_blocks, int32_t block_size, int32_t num_shards,
-                                dcp_ownership_t ownership, int32_t* local_block_table,
+                                int32_t ownership /* a dcp_ownership_t */, int32_t* local_block_table,
                                 int32_t* local_seq_lens, hipStream_t stream);
 
 /* Incremental form of dcp_block_remap (interleaved ownership) for a decode
@@ -201,7 +205,7 @@ dcp_status_t dcp_block_remap_update(const int32_t* block_table, const int32_t* o
  * skipped. Two tokens for the same slot in one call race. */
 dcp_status_t dcp_kv_append(const dcp_attn_desc_t* desc, int32_t num_tokens,
                            const int32_t* token_seq, const int32_t* positions, const void* k_new,
-                           const void* v_new, dcp_dtype_t new_dtype, int32_t shard,
+                           const void* v_new, int32_t new_dtype /* a dcp_dtype_t */, int32_t shard,
                            const int32_t* block_table, void* k_cache, void* v_cache,
                            float* kv_scale, hipStream_t stream);
 
@@ -287,7 +291,7 @@ dcp_status_t dcp_decode_partial_token(const dcp_attn_desc_t* desc, int32_t shard
  *   lse_out      [batch, num_heads] fp32, ln sum_i exp(LSE_i), or NULL */
 dcp_status_t dcp_lse_merge(const float* o_partials, const float* lse_partials,
                            int32_t num_partials, int32_t batch, int32_t num_heads, int32_t v_dim,
-                           void* out, dcp_dtype_t out_dtype, float* lse_out, hipStream_t stream);
+                           void* out, int32_t out_dtype /* a dcp_dtype_t */, float* lse_out, hipStream_t stream);
 
 /* All D shards of one layer on one GPU, fused: ownership j % D is applied on
  * the fly to the global block table, every shard's blocks are attended in
@@ -342,7 +346,7 @@ dcp_status_t dcp_decode_all_shards_noalloc(const dcp_attn_desc_t* desc, const vo
                                            hipStream_t stream);
 
 /* Static text for a status code. */
-const char* dcp_status_str(dcp_status_t status);
+const char* dcp_status_str(int32_t status /* a dcp_status_t */);
 
 /* Library version as major * 10000 + minor * 100 + patch. */
 int32_t dcp_version(void);

@@ -164,10 +164,31 @@ def components(dcp, desc, dev, w, ws, iters: int = 20):
     merge_bytes = (o_parts.numel() + lse_parts.numel() + out.numel() + lse.numel()) * 4
     slow = int(np.argmax(shard_ms))
 
-    def shard(r):
+    def shard(r, ms=None):
+        ms = shard_ms[r] if ms is None else ms
         b = int(shard_tokens[r]) * per_token
-        return {"shard": r, "ms": round(shard_ms[r], 4), "kv_bytes": b,
-                "GBps": round(b / (shard_ms[r] * 1e-3) / 1e9, 1)}
+        return {"shard": r, "ms": round(ms, 4), "kv_bytes": b,
+                "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
+
+    # Plan once per decode step, run per layer: the same shards' partials run
+    # on a plan made before the timed calls (every layer of a step shares the
+    # lengths, hence the plan).
+    ws_plan = dcp.alloc_workspace(desc, torch.device("cuda"))
+    run_ms = {}
+    for r in sorted({0, slow}):
+        ltr, llr = lt[r].contiguous(), ll[r].contiguous()
+        dcp.decode_partial_plan(desc, llr, ws_plan)
+        run_ms[r] = timed(lambda: dcp.decode_partial_run(
+            desc, dev.q, dev.k_cache, dev.v_cache, dev.kv_scale, ltr, ws_plan,
+            o_partial=o_parts[r], lse_partial=lse_parts[r]))
+    dcp.decode_all_shards_plan(desc, dev.seq_lens, ws_plan)
+    fused_out = torch.empty((spec.batch, spec.num_q_heads, spec.v_dim),
+                            dtype=torch.float32 if desc.out_dtype == dcp.F32 else torch.bfloat16,
+                            device="cuda")
+    fused_run_ms = timed(lambda: dcp.decode_all_shards_run(
+        desc, dev.q, dev.k_cache, dev.v_cache, dev.kv_scale, dev.block_table, ws_plan,
+        out=fused_out, want_lse=False))
+    fused_bytes = int(shard_tokens.sum()) * per_token
 
     # A decode step's cache maintenance: one new token per sequence, written at
     # the last position each table row maps, into a scratch pool of one block
@@ -194,12 +215,19 @@ def components(dcp, desc, dev, w, ws, iters: int = 20):
     upd_ms = timed(lambda: dcp.block_remap_update(dev.block_table, pos, dev.seq_lens,
                                                   spec.block_size, D, lt_u, ll_u))
     return {
-        "note": "per call, wall time of back-to-back calls; each dcp_decode_partial includes its own plan and piece merge",
+        "note": ("per call, wall time of back-to-back calls; each dcp_decode_partial includes its own "
+                 "plan and piece merge; the *_run entries run on a plan made once before them "
+                 "(dcp_decode_partial_plan / dcp_decode_all_shards_plan), as every layer of a "
+                 "decode step can"),
         "block_remap_ms": round(remap_ms, 4),
         "block_remap_update_ms": round(upd_ms, 4),
         "kv_append_ms": round(append_ms, 4),
         "decode_partial_shard0": shard(0),
         "decode_partial_slowest": shard(slow),
+        "decode_partial_run_shard0": shard(0, run_ms[0]),
+        "decode_partial_run_slowest": shard(slow, run_ms[slow]),
+        "decode_all_shards_run": {"ms": round(fused_run_ms, 4), "kv_bytes": fused_bytes,
+                                  "GBps": round(fused_bytes / (fused_run_ms * 1e-3) / 1e9, 1)},
         "lse_merge": {"partials": D, "ms": round(merge_ms, 4), "bytes": merge_bytes,
                       "GBps": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1)},
     }

@@ -29,7 +29,9 @@ import torch
 __all__ = [
     "AttnDesc", "DcpError", "LibraryMissing", "F32", "BF16", "FP8_E4M3", "KV_SEPARATE",
     "KV_LATENT", "OWN_INTERLEAVED", "OWN_CONTIGUOUS", "library_path", "lib", "make_desc", "block_remap", "block_remap_update", "kv_append", "workspace_size",
-    "decode_partial", "decode_partial_mtp", "lse_merge", "decode_all_shards", "status_str", "version",
+    "decode_partial", "decode_partial_mtp", "decode_partial_token", "decode_partial_plan",
+    "decode_partial_run", "lse_merge", "decode_all_shards", "decode_all_shards_plan",
+    "decode_all_shards_run", "decode_all_shards_noalloc", "status_str", "version",
 ]
 
 # The library the binding loads: the in-tree build, or the file named by the
@@ -131,6 +133,17 @@ def lib():
         L.dcp_decode_all_shards_noalloc.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P,
                                                     _P, _P, _P, _P]
         L.dcp_decode_all_shards_noalloc.restype = _I
+        L.dcp_decode_partial_plan.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, ctypes.c_size_t, _P]
+        L.dcp_decode_partial_plan.restype = _I
+        L.dcp_decode_partial_run.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P,
+                                             _P, ctypes.c_size_t, _P]
+        L.dcp_decode_partial_run.restype = _I
+        L.dcp_decode_all_shards_plan.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, ctypes.c_size_t,
+                                                 _P]
+        L.dcp_decode_all_shards_plan.restype = _I
+        L.dcp_decode_all_shards_run.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P,
+                                                _P, _P, ctypes.c_size_t, _P]
+        L.dcp_decode_all_shards_run.restype = _I
         L.dcp_status_str.argtypes = [_I]
         L.dcp_status_str.restype = ctypes.c_char_p
         L.dcp_version.argtypes = []
@@ -431,6 +444,59 @@ def decode_all_shards(desc: AttnDesc, q, k_cache, v_cache, kv_scale, block_table
             ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_scale),
             _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse_out), _ptr(workspace),
             workspace.numel(), _stream(dev), ev0.handle, ev1.handle))
+    return out, lse_out
+
+
+def decode_partial_plan(desc: AttnDesc, local_seq_lens, workspace: torch.Tensor):
+    """Plan one shard's partial for these local lengths into ``workspace``
+    (reused by decode_partial_run until the next plan on it)."""
+    _need(local_seq_lens, torch.int32, desc.batch)
+    _check(lib().dcp_decode_partial_plan(ctypes.byref(desc), _ptr(local_seq_lens), _ptr(workspace),
+                                         workspace.numel(), _stream(workspace.device)))
+    return workspace
+
+
+def decode_partial_run(desc: AttnDesc, q, k_cache, v_cache, kv_scale, local_block_table,
+                       workspace: torch.Tensor, o_partial: Optional[torch.Tensor] = None,
+                       lse_partial: Optional[torch.Tensor] = None):
+    """decode_partial on the plan in ``workspace`` (decode_partial_plan): the
+    lengths are the planned ones. Returns (O_r, LSE_r)."""
+    dev = q.device
+    rows = _rows(desc)
+    if o_partial is None:
+        o_partial = torch.empty((desc.batch, rows, desc.v_dim), dtype=torch.float32, device=dev)
+    if lse_partial is None:
+        lse_partial = torch.empty((desc.batch, rows), dtype=torch.float32, device=dev)
+    _check(lib().dcp_decode_partial_run(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(kv_scale), _ptr(local_block_table), _ptr(o_partial),
+                                        _ptr(lse_partial), _ptr(workspace), workspace.numel(),
+                                        _stream(dev)))
+    return o_partial, lse_partial
+
+
+def decode_all_shards_plan(desc: AttnDesc, seq_lens, workspace: torch.Tensor):
+    """Plan the fused all-shards call for these global lengths into ``workspace``."""
+    _need(seq_lens, torch.int32, desc.batch)
+    _check(lib().dcp_decode_all_shards_plan(ctypes.byref(desc), _ptr(seq_lens), _ptr(workspace),
+                                            workspace.numel(), _stream(workspace.device)))
+    return workspace
+
+
+def decode_all_shards_run(desc: AttnDesc, q, k_cache, v_cache, kv_scale, block_table,
+                          workspace: torch.Tensor, out: Optional[torch.Tensor] = None,
+                          lse_out: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """decode_all_shards on the plan in ``workspace`` (decode_all_shards_plan)."""
+    dev = q.device
+    rows = _rows(desc)
+    if out is None:
+        dt = torch.float32 if desc.out_dtype == F32 else torch.bfloat16
+        out = torch.empty((desc.batch, rows, desc.v_dim), dtype=dt, device=dev)
+    if lse_out is None and want_lse:
+        lse_out = torch.empty((desc.batch, rows), dtype=torch.float32, device=dev)
+    _check(lib().dcp_decode_all_shards_run(ctypes.byref(desc), _ptr(q), _ptr(k_cache),
+                                           _ptr(v_cache), _ptr(kv_scale), _ptr(block_table),
+                                           _ptr(out), _ptr(lse_out), _ptr(workspace),
+                                           workspace.numel(), _stream(dev)))
     return out, lse_out
 
 

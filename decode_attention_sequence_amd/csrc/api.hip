@@ -98,14 +98,20 @@ dcp_status_t check_tensors(const dcp_attn_desc_t* d, const void* q, const void* 
   return DCP_OK;
 }
 
+// What a call runs: the plan and the kernels that read it (one call), the plan
+// alone, or the kernels alone on a workspace planned before.
+enum class Phase { kAll, kPlan, kRun };
+
 // scale_ts: token stride of the fp8 scales (a token-interleave view's shard
 // count; else 1), scale_bs: their block stride in tokens (0: the block size).
+// The attention and merge kernels read the lengths the plan counted (its copy
+// in the workspace), never map.lens: a kRun call passes map.lens = null.
 dcp_status_t run_attention(const dcp_attn_desc_t* d, const void* q, const void* k, const void* v,
                            const float* kv_scale, const SegMap& map, int S, const Causal& cz,
                            void* out, dcp_dtype_t out_dtype, float* lse_out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream,
                            hipEvent_t attn_begin = nullptr, hipEvent_t attn_end = nullptr,
-                           int scale_ts = 1, int scale_bs = 0) {
+                           int scale_ts = 1, int scale_bs = 0, Phase phase = Phase::kAll) {
   const int G = groups_for(d);
   const int rows = desc_rows(d);
   const bool seq_pieces = d->kv_kind == DCP_KV_LATENT && mla_sequence_pieces(d, scale_ts);
@@ -117,17 +123,50 @@ dcp_status_t run_attention(const dcp_attn_desc_t* d, const void* q, const void* 
   WorkspaceView ws = carve_workspace(workspace, S, G, d->batch, rows, d->v_dim, seq_pieces);
   // Fixed work per piece of a segment, in blocks (about 128 tokens' worth).
   const int seg_cost = (128 + d->block_size - 1) / d->block_size;
-  if (launch_plan(m, S, G, seg_cost, rows, seq_pieces, ws, stream) != hipSuccess)
+  const PlanSig sig{kPlanMagic, S, G, d->batch, rows, seq_pieces ? 1 : 0,
+                    m.D, m.bs, m.width, m.tok_r, m.tok_D, d->v_dim};
+  if (phase != Phase::kRun &&
+      launch_plan(m, S, G, seg_cost, rows, seq_pieces, sig, ws, stream) != hipSuccess)
     return DCP_ERR_HIP;
-  AttnLaunch L{d, q, k, v, kv_scale, m, S, ws, cz, scale_bs > 0 ? scale_bs : d->block_size, scale_ts};
+  if (phase == Phase::kPlan) return DCP_OK;
+  m.lens = ws.lens;  // the lengths the plan counted
+  AttnLaunch L{d,  q,  k,  v, kv_scale, m, S, ws, cz, scale_bs > 0 ? scale_bs : d->block_size,
+               scale_ts, sig};
   if (attn_begin && hipEventRecord(attn_begin, stream) != hipSuccess) return DCP_ERR_HIP;
   hipError_t err = d->kv_kind == DCP_KV_LATENT ? launch_mla(L, stream) : launch_gqa(L, stream);
   if (err != hipSuccess) return DCP_ERR_HIP;
   if (attn_end && hipEventRecord(attn_end, stream) != hipSuccess) return DCP_ERR_HIP;
-  if (launch_merge_pieces(m, ws, G, rows, d->v_dim, out, out_dtype, lse_out, stream) !=
+  if (launch_merge_pieces(m, ws, sig, G, rows, d->v_dim, out, out_dtype, lse_out, stream) !=
       hipSuccess)
     return DCP_ERR_HIP;
   return DCP_OK;
+}
+
+// Segment maps: one shard's local table (one segment per sequence), and the
+// global table of all shards (segment s = sequence s / D, shard s % D).
+SegMap local_map(const dcp_attn_desc_t* d, const int32_t* table, const int32_t* lens) {
+  SegMap map;
+  map.table = table;
+  map.lens = lens;
+  map.width = (d->max_blocks_per_seq + d->num_shards - 1) / d->num_shards;
+  map.D = 1;
+  map.bs = d->block_size;
+  map.batch = d->batch;
+  map.tok_r = 0;
+  map.tok_D = 1;
+  return map;
+}
+SegMap global_map(const dcp_attn_desc_t* d, const int32_t* table, const int32_t* lens) {
+  SegMap map;
+  map.table = table;
+  map.lens = lens;
+  map.width = d->max_blocks_per_seq;
+  map.D = d->num_shards;
+  map.bs = d->block_size;
+  map.batch = d->batch;
+  map.tok_r = 0;
+  map.tok_D = 1;
+  return map;
 }
 
 // One shard's partial over its local table. q_pos null: single-token decode
@@ -144,15 +183,7 @@ dcp_status_t shard_partial(const dcp_attn_desc_t* d, int shard, const int32_t* q
     return DCP_ERR_INVALID_ARG;
   if (!aligned(o_partial, 16)) return DCP_ERR_INVALID_ARG;
   if (d->batch == 0) return DCP_OK;
-  SegMap map;
-  map.table = local_block_table;
-  map.lens = local_seq_lens;
-  map.width = (d->max_blocks_per_seq + d->num_shards - 1) / d->num_shards;
-  map.D = 1;
-  map.bs = d->block_size;
-  map.batch = d->batch;
-  map.tok_r = 0;
-  map.tok_D = 1;
+  const SegMap map = local_map(d, local_block_table, local_seq_lens);
   Causal cz{q_pos, q_pos ? desc_q_len(d) : 1, d->num_q_heads, shard, d->num_shards};
   return run_attention(d, q, k_cache, v_cache, kv_scale, map, d->batch, cz, o_partial, DCP_F32,
                        lse_partial, workspace, workspace_bytes, stream);
@@ -381,19 +412,72 @@ dcp_status_t dcp_decode_all_shards_timed(const dcp_attn_desc_t* d, const void* q
   if (!block_table || !seq_lens || !out) return DCP_ERR_INVALID_ARG;
   if (!aligned(out, d->out_dtype == DCP_F32 ? 16 : 8)) return DCP_ERR_INVALID_ARG;
   if (d->batch == 0) return DCP_OK;
-  SegMap map;
-  map.table = block_table;
-  map.lens = seq_lens;
-  map.width = d->max_blocks_per_seq;
-  map.D = d->num_shards;
-  map.bs = d->block_size;
-  map.batch = d->batch;
-  map.tok_r = 0;
-  map.tok_D = 1;
+  const SegMap map = global_map(d, block_table, seq_lens);
   const Causal cz{nullptr, desc_q_len(d), d->num_q_heads, 0, 1};
   return run_attention(d, q, k_cache, v_cache, kv_scale, map, d->batch * d->num_shards, cz, out,
                        static_cast<dcp_dtype_t>(d->out_dtype), lse_out, workspace, workspace_bytes,
                        stream, attn_begin, attn_end);
+}
+
+dcp_status_t dcp_decode_partial_plan(const dcp_attn_desc_t* d, const int32_t* local_seq_lens,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const dcp_status_t st = check_desc(d);
+  if (st != DCP_OK) return st;
+  if (desc_q_len(d) > 1 || !local_seq_lens) return DCP_ERR_INVALID_ARG;
+  if (d->batch == 0) return DCP_OK;
+  const Causal cz{nullptr, 1, d->num_q_heads, 0, d->num_shards};
+  return run_attention(d, nullptr, nullptr, nullptr, nullptr, local_map(d, nullptr, local_seq_lens),
+                       d->batch, cz, nullptr, DCP_F32, nullptr, workspace, workspace_bytes, stream,
+                       nullptr, nullptr, 1, 0, Phase::kPlan);
+}
+
+dcp_status_t dcp_decode_partial_run(const dcp_attn_desc_t* d, const void* q, const void* k_cache,
+                                    const void* v_cache, const float* kv_scale,
+                                    const int32_t* local_block_table, float* o_partial,
+                                    float* lse_partial, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  dcp_status_t st = check_desc(d);
+  if (st != DCP_OK) return st;
+  if (desc_q_len(d) > 1) return DCP_ERR_INVALID_ARG;
+  if ((st = check_tensors(d, q, k_cache, v_cache, kv_scale)) != DCP_OK) return st;
+  if (!local_block_table || !o_partial || !lse_partial) return DCP_ERR_INVALID_ARG;
+  if (!aligned(o_partial, 16)) return DCP_ERR_INVALID_ARG;
+  if (d->batch == 0) return DCP_OK;
+  const Causal cz{nullptr, 1, d->num_q_heads, 0, d->num_shards};
+  return run_attention(d, q, k_cache, v_cache, kv_scale, local_map(d, local_block_table, nullptr),
+                       d->batch, cz, o_partial, DCP_F32, lse_partial, workspace, workspace_bytes,
+                       stream, nullptr, nullptr, 1, 0, Phase::kRun);
+}
+
+dcp_status_t dcp_decode_all_shards_plan(const dcp_attn_desc_t* d, const int32_t* seq_lens,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  const dcp_status_t st = check_desc(d);
+  if (st != DCP_OK) return st;
+  if (!seq_lens) return DCP_ERR_INVALID_ARG;
+  if (d->batch == 0) return DCP_OK;
+  const Causal cz{nullptr, desc_q_len(d), d->num_q_heads, 0, 1};
+  return run_attention(d, nullptr, nullptr, nullptr, nullptr, global_map(d, nullptr, seq_lens),
+                       d->batch * d->num_shards, cz, nullptr, DCP_F32, nullptr, workspace,
+                       workspace_bytes, stream, nullptr, nullptr, 1, 0, Phase::kPlan);
+}
+
+dcp_status_t dcp_decode_all_shards_run(const dcp_attn_desc_t* d, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const float* kv_scale, const int32_t* block_table,
+                                       void* out, float* lse_out, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  dcp_status_t st = check_desc(d);
+  if (st != DCP_OK) return st;
+  if ((st = check_tensors(d, q, k_cache, v_cache, kv_scale)) != DCP_OK) return st;
+  if (!block_table || !out) return DCP_ERR_INVALID_ARG;
+  if (!aligned(out, d->out_dtype == DCP_F32 ? 16 : 8)) return DCP_ERR_INVALID_ARG;
+  if (d->batch == 0) return DCP_OK;
+  const Causal cz{nullptr, desc_q_len(d), d->num_q_heads, 0, 1};
+  return run_attention(d, q, k_cache, v_cache, kv_scale, global_map(d, block_table, nullptr),
+                       d->batch * d->num_shards, cz, out, static_cast<dcp_dtype_t>(d->out_dtype),
+                       lse_out, workspace, workspace_bytes, stream, nullptr, nullptr, 1, 0,
+                       Phase::kRun);
 }
 
 }  // extern "C"

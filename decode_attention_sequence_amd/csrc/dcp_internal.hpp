@@ -41,14 +41,37 @@ constexpr float kLn2 = 0.6931471805599453f;
 // is stored in slot s + g, which is unique because both s and g grow along
 // the concatenation. Slots used <= S + G - 1.
 // ---------------------------------------------------------------------------
+// Signature of a plan: the launch shape it was made for. The planning kernel
+// writes it into the workspace header; each kernel that reads a plan compares
+// it with its own launch's first and, when they differ, reads nothing of the
+// plan (attention: no work; piece merge: NaN outputs), so a workspace planned
+// for another shape, or never planned, is never taken for a plan.
+struct PlanSig {
+  int32_t magic;
+  int32_t S, G, B, rows, seq_pieces;
+  int32_t D, bs, width, tok_r, tok_D;
+  int32_t v_dim;
+};
+constexpr int32_t kPlanMagic = 0x31504344;  // "DCP1"
+
 struct PlanHeader {
   int32_t total;  // blocks over all segments
   int32_t pad[3];
   int32_t zero[4];  // 16 zero bytes: copy source for tile rows without a token
+  PlanSig sig;
 };
+
+__device__ __forceinline__ bool plan_matches(const PlanSig& want, const PlanHeader* hdr) {
+  const PlanSig h = hdr->sig;
+  return h.magic == want.magic && h.S == want.S && h.G == want.G && h.B == want.B &&
+         h.rows == want.rows && h.seq_pieces == want.seq_pieces && h.D == want.D &&
+         h.bs == want.bs && h.width == want.width && h.tok_r == want.tok_r &&
+         h.tok_D == want.tok_D && h.v_dim == want.v_dim;
+}
 // Workspace layout: PlanHeader, seg_off[S + 1], cost_off[S + 1],
-// wg_start[G + 1] and seq_slots[B][2] (int32), then at 256-byte alignment lse
-// slots [num_slots, Hq] fp32, then o slots [num_slots, Hq, v_dim] fp32.
+// wg_start[G + 1], seq_slots[B][2], wg_seg[G + 1] and lens[B] (int32), then at
+// 256-byte alignment lse slots [num_slots, Hq] fp32, then o slots [num_slots,
+// Hq, v_dim] fp32.
 
 struct SegMap {
   const int32_t* table;  // [B, width]
@@ -189,6 +212,8 @@ struct WorkspaceView {
   int32_t* cost_off;  // [S + 1] planning scratch: cost prefix sums
   int32_t* wg_start;  // [G + 1] first block of each work group's range
   int32_t* seq_slots; // [B][2] slot range [lo, hi) holding sequence b's pieces
+  int32_t* wg_seg;    // [G + 1] segment holding each range's first block
+  int32_t* lens;      // [B] the sequence lengths the plan was made with
   float* lse;
   float* o;
   int num_slots;
@@ -199,11 +224,14 @@ struct WorkspaceView {
 size_t workspace_bytes_for(int S, int G, int B, int Hq, int v_dim, bool seq_pieces);
 WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim, bool seq_pieces);
 
+// The plan also keeps a copy of the lengths it counted (ws.lens): the
+// attention and merge kernels of a launch read the lengths from there, so a
+// plan and the kernels that run it always agree on them.
 hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, int Hq, bool seq_pieces,
-                       WorkspaceView ws, hipStream_t stream);
-hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, int G, int Hq, int v_dim,
-                               void* out, dcp_dtype_t out_dtype, float* lse_out,
-                               hipStream_t stream);
+                       const PlanSig& sig, WorkspaceView ws, hipStream_t stream);
+hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, const PlanSig& sig, int G,
+                               int Hq, int v_dim, void* out, dcp_dtype_t out_dtype,
+                               float* lse_out, hipStream_t stream);
 hipError_t launch_merge_partials(const float* o, const float* lse, int P, int B, int H, int v_dim,
                                  void* out, dcp_dtype_t out_dtype, float* lse_out,
                                  hipStream_t stream);
@@ -255,6 +283,7 @@ struct AttnLaunch {
   // (scale_bs = block size, scale_ts = 1, except for a token-interleave view)
   int scale_bs;
   int scale_ts;
+  PlanSig sig;  // the plan this launch reads
 };
 
 // Query tokens per sequence and query rows per sequence of a descriptor (a

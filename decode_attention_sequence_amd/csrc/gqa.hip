@@ -35,7 +35,9 @@ struct GqaArgs {
   const char* v;
   SegMap map;
   const PlanHeader* hdr;
+  PlanSig sig;              // the plan's expected signature
   const int32_t* wg_start;  // [G + 1] block range of each work group
+  const int32_t* wg_seg;    // [G + 1] segment of each range's first block
   const int32_t* seg_off;
   float* ws_o;
   float* ws_lse;
@@ -92,10 +94,11 @@ __global__ __launch_bounds__(64) void gqa_bf16_kernel(GqaArgs a) {
   const int kvh = blockIdx.y / a.ctiles;
   const int ct = blockIdx.y - kvh * a.ctiles;
   const int g = xcd_logical_group(blockIdx.x, a.G);
+  if (!plan_matches(a.sig, a.hdr)) return;  // no plan of this launch's shape
   int pos = a.wg_start[g];
   const int end = a.wg_start[g + 1];
   if (pos >= end) return;
-  int s = find_segment(a.seg_off, a.S, pos);
+  int s = a.wg_seg[g];
   const int bs = a.map.bs;
   // This lane's query row: column 16ct + l16 of the KV head's (token, head) rows.
   const int col_q = 16 * ct + l16;
@@ -298,10 +301,11 @@ __global__ __launch_bounds__(64) void gqa_f32_kernel(GqaArgs a) {
   const int kvh = blockIdx.y / a.ctiles;
   const int ct = blockIdx.y - kvh * a.ctiles;
   const int g = xcd_logical_group(blockIdx.x, a.G);
+  if (!plan_matches(a.sig, a.hdr)) return;  // no plan of this launch's shape
   int pos = a.wg_start[g];
   const int end = a.wg_start[g + 1];
   if (pos >= end) return;
-  int s = find_segment(a.seg_off, a.S, pos);
+  int s = a.wg_seg[g];
   const int bs = a.map.bs;
   // Columns j < G of this wave: the KV head's query rows 16ct + j (token, head).
   const int G = min(kMaxGroup, a.cols - 16 * ct);
@@ -426,7 +430,9 @@ hipError_t launch_gqa(const AttnLaunch& L, hipStream_t stream) {
   a.v = static_cast<const char*>(L.v_cache);
   a.map = L.map;
   a.hdr = L.ws.header;
+  a.sig = L.sig;
   a.wg_start = L.ws.wg_start;
+  a.wg_seg = L.ws.wg_seg;
   a.seg_off = L.ws.seg_off;
   a.ws_o = L.ws.o;
   a.ws_lse = L.ws.lse;

@@ -83,7 +83,9 @@ struct MlaArgs {
   int scale_bs, scale_ts;
   SegMap map;
   const PlanHeader* hdr;
+  PlanSig sig;              // the plan's expected signature
   const int32_t* wg_start;  // [G + 1] block range of each work group
+  const int32_t* wg_seg;    // [G + 1] segment of each range's first block
   const int32_t* seg_off;
   float* ws_o;
   float* ws_lse;
@@ -379,10 +381,11 @@ __global__ __launch_bounds__(2 * HG * 64) void mla_partial_kernel(MlaArgs a) {
   const int l16 = lane & 15;
   const int g = xcd_logical_group(blockIdx.x, kGroups);
   const int head0 = blockIdx.y * 16 * HG;
+  if (!plan_matches(a.sig, a.hdr)) return;  // no plan of this launch's shape
   int pos = a.wg_start[g];
   const int end = a.wg_start[g + 1];
   if (pos >= end) return;
-  int s = find_segment(a.seg_off, a.S, pos);
+  int s = a.wg_seg[g];
   const int bs = a.map.bs;
   const int h_s = head0 + 16 * hg + l16;  // head of this lane's scores
   const uint32_t flags_addr = aux_addr + C::kFlagOff;
@@ -1042,6 +1045,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
   const int k8 = blockIdx.x >> 3;
   const int g = (blockIdx.x & 7) * (kGroups >> 3) + k8 / ngrp;
   const int head0 = (k8 % ngrp) * 64;
+  if (!plan_matches(a.sig, a.hdr)) return;  // no plan of this launch's shape
   const int total = a.hdr->total;
   const int range0 = a.wg_start[g];
   const int end = a.wg_start[g + 1];
@@ -1293,7 +1297,7 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
     int nfin = 0;             // segments finished so far (parity selects the fin buffer)
 
     int wpos = range0;
-    int s_cur = find_segment(a.seg_off, a.S, wpos);
+    int s_cur = a.wg_seg[g];
     while (wpos < end) {
       // ---- window [wpos, wend): piece table (wave 0), then tile table (all)
       if (w == 0) {
@@ -1968,7 +1972,9 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   a.scale_ts = L.scale_ts;
   a.map = L.map;
   a.hdr = L.ws.header;
+  a.sig = L.sig;
   a.wg_start = L.ws.wg_start;
+  a.wg_seg = L.ws.wg_seg;
   a.seg_off = L.ws.seg_off;
   a.ws_o = L.ws.o;
   a.ws_lse = L.ws.lse;

@@ -17,7 +17,8 @@ static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; 
 
 static inline size_t plan_bytes(int S, int G, int B) {
   return sizeof(PlanHeader) + sizeof(int32_t) * (2 * (static_cast<size_t>(S) + 1) +
-                                                 static_cast<size_t>(G) + 1 + 2 * static_cast<size_t>(B));
+                                                 2 * (static_cast<size_t>(G) + 1) +
+                                                 3 * static_cast<size_t>(B));
 }
 
 static inline int slot_count(int S, int G, int B, bool seq_pieces) {
@@ -41,6 +42,8 @@ WorkspaceView carve_workspace(void* ws, int S, int G, int B, int Hq, int v_dim, 
   v.cost_off = v.seg_off + S + 1;
   v.wg_start = v.cost_off + S + 1;
   v.seq_slots = v.wg_start + G + 1;
+  v.wg_seg = v.seq_slots + 2 * B;
+  v.lens = v.wg_seg + G + 1;
   size_t off = align_up(plan_bytes(S, G, B), 256);
   v.lse = reinterpret_cast<float*>(base + off);
   off += align_up(static_cast<size_t>(v.num_slots) * Hq * sizeof(float), 256);
@@ -75,7 +78,8 @@ __device__ __forceinline__ int split_start(int total_c, int G, int g) {
 __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int seg_cost, int Hq,
                                                     int seq_pieces, PlanHeader* hdr, int32_t* seg_off,
                                                     int32_t* cost_off, int32_t* wg_start,
-                                                    int32_t* seq_slots, float* lse) {
+                                                    int32_t* seq_slots, int32_t* wg_seg,
+                                                    int32_t* lens, PlanSig sig, float* lse) {
   __shared__ int w_sum[16];
   __shared__ int w_cost[16];
   __shared__ int l_seg[kPlanLds];
@@ -140,7 +144,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
     l_cost[0] = 0;
   }
   if (t < 4) hdr->zero[t] = 0;
-  if (t == 0) hdr->total = total;
+  if (t == 0) {
+    hdr->total = total;
+    hdr->sig = sig;
+  }
+  // The lengths this plan counted, for the kernels that run it.
+  for (int b = t; b < m.batch; b += 1024) lens[b] = m.lens[b];
   __syncthreads();  // seg_off and cost_off complete
   const int* so = mirror_s ? l_seg : seg_off;
   const int* co = mirror_s ? l_cost : cost_off;
@@ -162,6 +171,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
     }
     wg_start[g] = g == 0 ? 0 : x;
     if (mirror_g) l_wg[g] = g == 0 ? 0 : x;
+    // The segment of the range's first block, so that a work group starts
+    // without searching seg_off (ranges past the last block never read it).
+    const int x0 = g == 0 ? 0 : x;
+    wg_seg[g] = x0 < total ? find_segment(so, S, x0) : 0;
   }
   // The work group of block i of segment s is the range holding its cost
   // position cost_off[s] + seg_cost + i (the same split as above): the last g
@@ -246,10 +259,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
 }
 
 hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, int Hq, bool seq_pieces,
-                       WorkspaceView ws, hipStream_t stream) {
+                       const PlanSig& sig, WorkspaceView ws, hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, m, S, G, seg_cost, Hq,
                      seq_pieces ? 1 : 0, ws.header,
-                     ws.seg_off, ws.cost_off, ws.wg_start, ws.seq_slots, ws.lse);
+                     ws.seg_off, ws.cost_off, ws.wg_start, ws.seq_slots, ws.wg_seg, ws.lens, sig,
+                     ws.lse);
   return hipGetLastError();
 }
 
@@ -258,6 +272,9 @@ hipError_t launch_plan(const SegMap& m, int S, int G, int seg_cost, int Hq, bool
 // the i-th at row slot(b, i); a row whose LSE is -inf is empty.
 struct PieceSource {
   const int32_t* seq_slots;  // [B][2] contiguous slot range of each sequence
+  const PlanHeader* hdr;
+  PlanSig sig;
+  __device__ __forceinline__ bool valid() const { return plan_matches(sig, hdr); }
   __device__ __forceinline__ int first(int b) const { return seq_slots[2 * b]; }
   __device__ __forceinline__ int count(int b) const { return seq_slots[2 * b + 1] - seq_slots[2 * b]; }
   __device__ __forceinline__ int slot(int b, int i, int first) const { return first + i; }
@@ -265,6 +282,7 @@ struct PieceSource {
 
 struct PartialSource {
   int P, B;
+  __device__ __forceinline__ bool valid() const { return true; }
   __device__ __forceinline__ int first(int) const { return 0; }
   __device__ __forceinline__ int count(int) const { return P; }
   __device__ __forceinline__ int slot(int b, int i, int) const { return i * B + b; }
@@ -279,7 +297,10 @@ struct PartialSource {
 // trip for up to kMergeRows partials. Rows past the count are not loaded; the
 // row of an empty partial (LSE = -inf) is dropped by a select, so garbage in
 // it never reaches the sum.
-constexpr int kMergeRows = 16;      // partial rows in flight per thread
+// Eight rows keep the kernel at 64 VGPRs, so eight waves fit on every SIMD and
+// one round of work groups covers the usual grids (2048 groups of 256 threads);
+// sixteen rows took 102 VGPRs and two rounds.
+constexpr int kMergeRows = 8;       // partial rows in flight per thread
 constexpr int kMergeThreads = 256;  // threads per work group
 
 // Heads per merge work group for a value width (v_dim / 4 threads per head).
@@ -301,6 +322,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   const int b = blockIdx.y;
   const int h = blockIdx.x * hpb + hh;
   if (hh >= hpb || h >= H) return;  // (no barriers below)
+  const size_t oidx = (static_cast<size_t>(b) * H + h) * v_dim + 4 * v4;
+  if (!src.valid()) {
+    // The workspace holds no plan of this launch's shape: NaN outputs.
+    if (out_bf16)
+      *reinterpret_cast<i32x2*>(static_cast<uint16_t*>(out) + oidx) = i32x2{0x7fc07fc0, 0x7fc07fc0};
+    else
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + oidx) = f32x4{NAN, NAN, NAN, NAN};
+    if (lse_out && v4 == 0) lse_out[static_cast<size_t>(b) * H + h] = NAN;
+    return;
+  }
   const int n = src.count(b);
   const int f0 = src.first(b);
   const float* orow = o_rows + static_cast<size_t>(h) * v_dim + 4 * v4;
@@ -325,10 +356,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     for (int u = 0; u < kMergeRows; ++u) mr = fmaxf(mr, l[u]);
     if (mr == -INFINITY) continue;  // only empty partials so far
     const float ml = mr * kLog2e;
-    const float alpha = m == -INFINITY ? 0.f : fast_exp2(m * kLog2e - ml);
-    acc *= alpha;
-    wsum *= alpha;
-    m = mr;
+    if (mr != m) {
+      // (Only when the maximum rises: a round of empty partials leaves the sums
+      // exactly as they are.)
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2(m * kLog2e - ml);
+      acc *= alpha;
+      wsum *= alpha;
+      m = mr;
+    }
 #pragma unroll
     for (int u = 0; u < kMergeRows; ++u) {
       const bool on = l[u] != -INFINITY;
@@ -339,7 +374,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     }
   }
   if (m != -INFINITY) acc *= 1.0f / wsum;
-  const size_t oidx = (static_cast<size_t>(b) * H + h) * v_dim + 4 * v4;
   if (out_bf16) {
     uint16_t* o16 = static_cast<uint16_t*>(out) + oidx;
     uint32_t lo = f32_to_bf16_bits(acc[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[1])) << 16);
@@ -352,11 +386,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     lse_out[static_cast<size_t>(b) * H + h] = m == -INFINITY ? -INFINITY : m + fast_log2(wsum) * kLn2;
 }
 
-hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, int G, int Hq, int v_dim,
-                               void* out, dcp_dtype_t out_dtype, float* lse_out,
-                               hipStream_t stream) {
+hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, const PlanSig& sig, int G,
+                               int Hq, int v_dim, void* out, dcp_dtype_t out_dtype,
+                               float* lse_out, hipStream_t stream) {
   (void)G;
-  PieceSource src{ws.seq_slots};
+  PieceSource src{ws.seq_slots, ws.header, sig};
   const int hpb = merge_heads(v_dim);
   dim3 grid((Hq + hpb - 1) / hpb, m.batch);
   hipLaunchKernelGGL(merge_kernel<PieceSource>, grid, dim3(kMergeThreads), 0, stream,

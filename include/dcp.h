@@ -324,6 +324,49 @@ dcp_status_t dcp_decode_all_shards_timed(const dcp_attn_desc_t* desc, const void
                                          hipStream_t stream, hipEvent_t attn_begin,
                                          hipEvent_t attn_end);
 
+/* Plan once, run per layer. A call of dcp_decode_partial or
+ * dcp_decode_all_shards first plans its work (a small kernel that splits the
+ * shards' blocks into equal ranges, one per work group, from the sequence
+ * lengths) and then runs attention and merge. The plan depends only on the
+ * descriptor's shape fields and the lengths, which every layer of a decode
+ * step shares, so a model computes it once per step and runs each layer on it
+ * -- as "vLLM长序列推理优化" (section 6.2) has the block-table remap computed
+ * once and reused until the tables change.
+ *
+ * dcp_decode_partial_plan / dcp_decode_all_shards_plan write the plan for
+ * `desc` and the given lengths into `workspace` (sized by
+ * dcp_workspace_size(desc)), together with a copy of the lengths.
+ * dcp_decode_partial_run / dcp_decode_all_shards_run then compute exactly what
+ * dcp_decode_partial / dcp_decode_all_shards would for those lengths (bit for
+ * bit), reading the block table, query and cache as they are at run time;
+ * their other arguments are those of the unplanned calls, without the
+ * lengths. Any number of runs, with any queries and caches of the same shape,
+ * may follow one plan on the same workspace, in stream order.
+ *
+ * Ownership: the workspace holds the plan until the next plan or unplanned
+ * call on it. Errors: the host checks are those of the unplanned calls. The
+ * workspace records the shape its plan was made for (batch, heads, query
+ * rows, v_dim, block size, table width, shard count); a run whose descriptor
+ * differs in any of them, or a run on a workspace that holds no plan, reads
+ * none of it and writes NaN to every output (and LSE) value instead. A run
+ * after the caller changed the lengths without planning again uses the
+ * planned lengths. */
+dcp_status_t dcp_decode_partial_plan(const dcp_attn_desc_t* desc, const int32_t* local_seq_lens,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+dcp_status_t dcp_decode_partial_run(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
+                                    const void* v_cache, const float* kv_scale,
+                                    const int32_t* local_block_table, float* o_partial,
+                                    float* lse_partial, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+dcp_status_t dcp_decode_all_shards_plan(const dcp_attn_desc_t* desc, const int32_t* seq_lens,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+dcp_status_t dcp_decode_all_shards_run(const dcp_attn_desc_t* desc, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const float* kv_scale, const int32_t* block_table,
+                                       void* out, float* lse_out, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of the device scratch array behind dcp_decode_all_shards_noalloc. */
 #define DCP_NOALLOC_SCRATCH_BYTES (64u << 20)
 

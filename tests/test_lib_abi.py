@@ -257,3 +257,42 @@ def test_token_partial_argument_errors():
     assert call_partial_token(mla_desc(), 8) == dcp.DCP_ERR_INVALID_ARG
     assert call_partial_token(mla_desc(q_len=2), 0) == dcp.DCP_ERR_INVALID_ARG
     assert call_partial_token(mla_desc(), 0, ws_bytes=16) == dcp.DCP_ERR_WORKSPACE
+
+
+def test_plan_and_run_argument_errors():
+    """Plan / run entry points: the unplanned calls' host checks, all rejected
+    before anything is enqueued (every workspace here is too small to plan in)."""
+    L = dcp.lib()
+
+    def pplan(desc, lens=FAKE, n=16):
+        return L.dcp_decode_partial_plan(ctypes.byref(desc), lens, FAKE, n, None)
+
+    def prun(desc, q=FAKE, table=FAKE, o=FAKE, lse=FAKE, n=16):
+        return L.dcp_decode_partial_run(ctypes.byref(desc), q, FAKE, FAKE, FAKE, table, o, lse,
+                                        FAKE, n, None)
+
+    def aplan(desc, lens=FAKE, n=16):
+        return L.dcp_decode_all_shards_plan(ctypes.byref(desc), lens, FAKE, n, None)
+
+    def arun(desc, q=FAKE, table=FAKE, out=FAKE, n=16):
+        return L.dcp_decode_all_shards_run(ctypes.byref(desc), q, FAKE, FAKE, FAKE, table, out,
+                                           FAKE, FAKE, n, None)
+
+    d = mla_desc()
+    for call in (pplan, prun, aplan, arun):
+        assert call(d) == dcp.DCP_ERR_WORKSPACE
+        assert call(mla_desc(num_q_heads=0)) == dcp.DCP_ERR_INVALID_ARG
+        assert call(mla_desc(out_dtype=dcp.FP8_E4M3)) == dcp.DCP_ERR_UNSUPPORTED
+    assert pplan(d, lens=None) == dcp.DCP_ERR_INVALID_ARG
+    assert aplan(d, lens=None) == dcp.DCP_ERR_INVALID_ARG
+    assert pplan(mla_desc(q_len=2)) == dcp.DCP_ERR_INVALID_ARG
+    assert prun(mla_desc(q_len=2)) == dcp.DCP_ERR_INVALID_ARG
+    assert prun(d, q=None) == dcp.DCP_ERR_INVALID_ARG
+    assert prun(d, table=None) == dcp.DCP_ERR_INVALID_ARG
+    assert prun(d, o=None) == dcp.DCP_ERR_INVALID_ARG
+    assert prun(d, lse=None) == dcp.DCP_ERR_INVALID_ARG
+    assert prun(d, o=ctypes.c_void_p((1 << 20) + 4)) == dcp.DCP_ERR_INVALID_ARG
+    assert arun(d, q=None) == dcp.DCP_ERR_INVALID_ARG
+    assert arun(d, table=None) == dcp.DCP_ERR_INVALID_ARG
+    assert arun(d, out=None) == dcp.DCP_ERR_INVALID_ARG
+    assert arun(gqa_desc(), n=16) == dcp.DCP_ERR_WORKSPACE

@@ -131,11 +131,9 @@ dcp_status_t run_attention(const dcp_attn_desc_t* d, const void* q, const void* 
   if (phase == Phase::kPlan) return DCP_OK;
   m.lens = ws.lens;  // the lengths the plan counted
   AttnLaunch L{d,  q,  k,  v, kv_scale, m, S, ws, cz, scale_bs > 0 ? scale_bs : d->block_size,
-               scale_ts, sig};
-  if (attn_begin && hipEventRecord(attn_begin, stream) != hipSuccess) return DCP_ERR_HIP;
+               scale_ts, sig, attn_begin, attn_end};
   hipError_t err = d->kv_kind == DCP_KV_LATENT ? launch_mla(L, stream) : launch_gqa(L, stream);
   if (err != hipSuccess) return DCP_ERR_HIP;
-  if (attn_end && hipEventRecord(attn_end, stream) != hipSuccess) return DCP_ERR_HIP;
   if (launch_merge_pieces(m, ws, sig, G, rows, d->v_dim, out, out_dtype, lse_out, stream) !=
       hipSuccess)
     return DCP_ERR_HIP;

@@ -1,6 +1,7 @@
 // Internal declarations shared by the libdcp translation units (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -284,6 +285,11 @@ struct AttnLaunch {
   int scale_bs;
   int scale_ts;
   PlanSig sig;  // the plan this launch reads
+  // Optional events that the attention kernel's own dispatch records at its
+  // start and end (hipExtLaunchKernel): the kernel's duration without the
+  // marker packets a separate hipEventRecord puts between the kernels.
+  hipEvent_t ev_begin = nullptr;
+  hipEvent_t ev_end = nullptr;
 };
 
 // Query tokens per sequence and query rows per sequence of a descriptor (a

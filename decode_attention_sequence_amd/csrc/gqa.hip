@@ -453,14 +453,18 @@ hipError_t launch_gqa(const AttnLaunch& L, hipStream_t stream) {
   const dim3 grid(a.G, d->num_kv_heads * a.ctiles);
   if (d->kv_dtype == DCP_BF16) {
     if (d->qk_dim == 128)
-      hipLaunchKernelGGL(gqa_bf16_kernel<128>, grid, dim3(64), 0, stream, a);
+      hipExtLaunchKernelGGL(gqa_bf16_kernel<128>, grid, dim3(64), 0, stream, L.ev_begin, L.ev_end,
+                            0, a);
     else
-      hipLaunchKernelGGL(gqa_bf16_kernel<64>, grid, dim3(64), 0, stream, a);
+      hipExtLaunchKernelGGL(gqa_bf16_kernel<64>, grid, dim3(64), 0, stream, L.ev_begin, L.ev_end,
+                            0, a);
   } else {
     if (d->qk_dim == 128)
-      hipLaunchKernelGGL(gqa_f32_kernel<128>, grid, dim3(64), 0, stream, a);
+      hipExtLaunchKernelGGL(gqa_f32_kernel<128>, grid, dim3(64), 0, stream, L.ev_begin, L.ev_end,
+                            0, a);
     else
-      hipLaunchKernelGGL(gqa_f32_kernel<64>, grid, dim3(64), 0, stream, a);
+      hipExtLaunchKernelGGL(gqa_f32_kernel<64>, grid, dim3(64), 0, stream, L.ev_begin, L.ev_end,
+                            0, a);
   }
   return hipGetLastError();
 }

@@ -1955,11 +1955,14 @@ bool mla_sequence_pieces(const dcp_attn_desc_t* d, int scale_ts) {
 }
 
 template <int HG, bool FP8>
-static void launch_mla_hg(const MlaArgs& a, bool bs32, dim3 grid, hipStream_t stream) {
+static void launch_mla_hg(const MlaArgs& a, bool bs32, dim3 grid, hipStream_t stream,
+                          hipEvent_t e0, hipEvent_t e1) {
   if (bs32)
-    hipLaunchKernelGGL((mla_partial_kernel<HG, FP8, true>), grid, dim3(2 * HG * 64), 0, stream, a);
+    hipExtLaunchKernelGGL((mla_partial_kernel<HG, FP8, true>), grid, dim3(2 * HG * 64), 0, stream,
+                          e0, e1, 0, a);
   else
-    hipLaunchKernelGGL((mla_partial_kernel<HG, FP8, false>), grid, dim3(2 * HG * 64), 0, stream, a);
+    hipExtLaunchKernelGGL((mla_partial_kernel<HG, FP8, false>), grid, dim3(2 * HG * 64), 0, stream,
+                          e0, e1, 0, a);
 }
 
 hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
@@ -1998,26 +2001,34 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
     const int ngrp = a.Hq / 64;
     const dim3 pgrid(kGroups * ngrp);
     if (ngrp > 1) {
-      if (fp8) hipLaunchKernelGGL((mla_pp_kernel<true, true>), pgrid, dim3(512), 0, stream, a);
-      else hipLaunchKernelGGL((mla_pp_kernel<false, true>), pgrid, dim3(512), 0, stream, a);
+      if (fp8)
+        hipExtLaunchKernelGGL((mla_pp_kernel<true, true>), pgrid, dim3(512), 0, stream, L.ev_begin,
+                              L.ev_end, 0, a);
+      else
+        hipExtLaunchKernelGGL((mla_pp_kernel<false, true>), pgrid, dim3(512), 0, stream,
+                              L.ev_begin, L.ev_end, 0, a);
     } else {
-      if (fp8) hipLaunchKernelGGL((mla_pp_kernel<true, false>), pgrid, dim3(512), 0, stream, a);
-      else hipLaunchKernelGGL((mla_pp_kernel<false, false>), pgrid, dim3(512), 0, stream, a);
+      if (fp8)
+        hipExtLaunchKernelGGL((mla_pp_kernel<true, false>), pgrid, dim3(512), 0, stream,
+                              L.ev_begin, L.ev_end, 0, a);
+      else
+        hipExtLaunchKernelGGL((mla_pp_kernel<false, false>), pgrid, dim3(512), 0, stream,
+                              L.ev_begin, L.ev_end, 0, a);
     }
     return hipGetLastError();
   }
   switch (heads / 16) {
     case 1:
-      if (fp8) launch_mla_hg<1, true>(a, bs32, grid, stream);
-      else launch_mla_hg<1, false>(a, bs32, grid, stream);
+      if (fp8) launch_mla_hg<1, true>(a, bs32, grid, stream, L.ev_begin, L.ev_end);
+      else launch_mla_hg<1, false>(a, bs32, grid, stream, L.ev_begin, L.ev_end);
       break;
     case 2:
-      if (fp8) launch_mla_hg<2, true>(a, bs32, grid, stream);
-      else launch_mla_hg<2, false>(a, bs32, grid, stream);
+      if (fp8) launch_mla_hg<2, true>(a, bs32, grid, stream, L.ev_begin, L.ev_end);
+      else launch_mla_hg<2, false>(a, bs32, grid, stream, L.ev_begin, L.ev_end);
       break;
     case 4:
-      if (fp8) launch_mla_hg<4, true>(a, bs32, grid, stream);
-      else launch_mla_hg<4, false>(a, bs32, grid, stream);
+      if (fp8) launch_mla_hg<4, true>(a, bs32, grid, stream, L.ev_begin, L.ev_end);
+      else launch_mla_hg<4, false>(a, bs32, grid, stream, L.ev_begin, L.ev_end);
       break;
     default:
       return hipErrorInvalidValue;

@@ -313,9 +313,10 @@ dcp_status_t dcp_decode_all_shards(const dcp_attn_desc_t* desc, const void* q, c
 
 /* dcp_decode_all_shards with timing hooks for profilers and benchmarks: the
  * same work, plus `attn_begin` / `attn_end` (events created by the caller)
- * recorded on `stream` immediately before and after the attention kernel,
- * so hipEventElapsedTime gives that kernel's duration alone. Either event may
- * be NULL. */
+ * that the attention kernel's dispatch itself records at the kernel's start
+ * and end (hipExtLaunchKernel), so hipEventElapsedTime gives that kernel's
+ * duration alone and no marker is queued between the kernels. Either event
+ * may be NULL. */
 dcp_status_t dcp_decode_all_shards_timed(const dcp_attn_desc_t* desc, const void* q,
                                          const void* k_cache, const void* v_cache,
                                          const float* kv_scale, const int32_t* block_table,

@@ -18,7 +18,11 @@
  *    never allocates, frees or keeps pointers after the enqueued work ends.
  *  - Every call only enqueues work on `stream` (0 = the default stream) and
  *    returns without synchronising, so calls can be captured in a HIP graph.
- *    The library keeps no mutable global state and is thread-safe.
+ *    The library keeps no mutable global state and is thread-safe, except
+ *    for the static device scratch array of dcp_decode_all_shards_noalloc
+ *    (one per GPU, shared by that entry point's calls). A workspace holds
+ *    what the caller last planned into it (the *_plan entry points) until the
+ *    next call on it.
  *  - Host-visible arguments are validated before anything is enqueued; on an
  *    error nothing is enqueued and the call returns a non-zero status.
  *    DCP_ERR_HIP reports a launch error from the HIP runtime.

@@ -159,3 +159,48 @@ def test_run_without_a_matching_plan_writes_nan():
     o_ref, lse_ref = oracle.decode_reference(w)
     rows = np.arange(spec.batch - 1)
     compare(o, l, o_ref[rows], lse_ref[rows], **TOL["bf16"], label="replanned")
+
+
+@pytest.mark.parametrize("spec", [W.scaled(W.SPECS["mla_bf16_b64_bimodal"], 16, 128),
+                                  W.scaled(W.SPECS["gqa_bf16_b32_L32k"], 8, 64)],
+                         ids=lambda s: s.name)
+def test_run_captured_in_a_graph_follows_each_new_plan(spec):
+    """The run alone captured in a HIP graph, the plan made eagerly before each
+    replay: every replay computes what the unplanned call computes for the
+    lengths of the latest plan and the query in the buffer at replay time, so
+    one captured graph serves decode steps whose lengths change."""
+    w = W.make(spec)
+    dev = W.to_torch(w)
+    desc = desc_for(w, dev)
+    ws = dcp.alloc_workspace(desc, "cuda")
+    rows = spec.q_len * spec.num_q_heads
+    out = torch.empty((spec.batch, rows, spec.v_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((spec.batch, rows), dtype=torch.float32, device="cuda")
+    q = dev.q.clone()
+
+    def run():
+        dcp.decode_all_shards_run(desc, q, dev.k_cache, dev.v_cache, dev.kv_scale,
+                                  dev.block_table, ws, out=out, lse_out=lse)
+
+    dcp.decode_all_shards_plan(desc, dev.seq_lens, ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    lens_steps = [dev.seq_lens, torch.clamp(dev.seq_lens - 7, min=0),
+                  torch.div(dev.seq_lens, 2, rounding_mode="floor")]
+    for i, lens in enumerate(lens_steps):
+        lens = lens.to(torch.int32).contiguous()
+        q.copy_(dev.q if i % 2 == 0 else -dev.q)
+        dcp.decode_all_shards_plan(desc, lens, ws)
+        out.fill_(float("nan"))
+        graph.replay()
+        o_ref, l_ref = dcp.decode_all_shards(desc, q, dev.k_cache, dev.v_cache, dev.kv_scale,
+                                             dev.block_table, lens)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(lse, l_ref), f"step {i}"

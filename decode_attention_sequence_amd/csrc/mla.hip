@@ -1243,12 +1243,17 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
 #pragma unroll
       for (int nt = 0; nt < kQTiles; ++nt) {
         const int head = FP8 ? head0 + 32 * hp + 16 * nt + l16 : head0 + 16 * grp + l16;
+        // (With 16 or 32 query rows the rows past them are zero queries whose
+        // results are never stored.)
+        const bool real = head < a.Hq;
         const uint16_t* qrow =
-            a.q + (static_cast<size_t>(b) * a.Hq + head) * kQK + (FP8 ? 16 : 8) * q4;
+            a.q + (static_cast<size_t>(b) * a.Hq + (real ? head : 0)) * kQK + (FP8 ? 16 : 8) * q4;
 #pragma unroll
         for (int kk = 0; kk < kKSteps; ++kk) {
           const int col = FP8 ? 64 * (kk >> 1) + 8 * (kk & 1) : 32 * kk;
-          st[nt * kKSteps + kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + col));
+          bf16x8 v = {};
+          if (real) v = *reinterpret_cast<const bf16x8*>(qrow + col);
+          st[nt * kKSteps + kk] = __builtin_bit_cast(f32x4, v);
         }
       }
       // Consume the loads here, in order: the compiler then waits for exactly
@@ -1680,12 +1685,13 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
               const float lt = __int_as_float(h0[nt]) + __int_as_float(h1[nt]);
               const float inv = lt > 0.f ? 1.f / lt : 0.f;
               float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
+              const bool real = head0 + 16 * nt < a.Hq;  // (rows past 16 or 32 query rows)
 #pragma unroll
               for (int mt = 0; mt < P::kMT; ++mt) {
-                *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
+                if (real) *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
                 st[4 * mt + nt] = f32x4{0.f, 0.f, 0.f, 0.f};
               }
-              if (grp == 0 && q4 == 0)
+              if (real && grp == 0 && q4 == 0)
                 a.ws_lse[slot * a.Hq + head0 + 16 * nt + l16] =
                     lt > 0.f ? (__int_as_float(mm[nt]) + fast_log2(lt)) * kLn2 : -INFINITY;
             }
@@ -1788,8 +1794,9 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             if (q4 == 0) {
               lds_store_b32(aux_addr + P::kFinOff + ((nfin & 1) * 64 + 16 * grp + l16) * 4, l_o);
               const size_t slot = static_cast<size_t>(piece_b(ti.piece())) + g;
-              a.ws_lse[slot * a.Hq + head0 + 16 * grp + l16] =
-                  l_h > 0.f ? (m_ref + fast_log2(l_h)) * kLn2 : -INFINITY;
+              if (head0 + 16 * grp < a.Hq)  // (rows past 16 or 32 query rows)
+                a.ws_lse[slot * a.Hq + head0 + 16 * grp + l16] =
+                    l_h > 0.f ? (m_ref + fast_log2(l_h)) * kLn2 : -INFINITY;
             }
             ++nfin;
           }
@@ -1897,9 +1904,10 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             for (int nt = 0; nt < 4; ++nt) {
               const float inv = lt[nt] > 0.f ? 1.f / lt[nt] : 0.f;
               float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
+              const bool real = head0 + 16 * nt < a.Hq;  // (rows past 16 or 32 query rows)
 #pragma unroll
               for (int mt = 0; mt < P::kMT; ++mt) {
-                *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
+                if (real) *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
                 st[4 * mt + nt] = f32x4{0.f, 0.f, 0.f, 0.f};
               }
             }
@@ -1937,11 +1945,17 @@ bool mla_supported(const dcp_attn_desc_t* d) {
 // general kernel. A tile's address is block id * block stride (the stride
 // below 4 GiB) plus its offset in the block (the block's rows below 4 GiB).
 // Multi-token decode needs each 64-row head group to hold one query token.
+// Single-token decode with 16 or 32 query heads runs as one 64-row group
+// padded with zero queries whose results are not stored: on MI355X that takes
+// the 64-head time (bimodal batch, fp8: 1.6 ms), where the general kernel took
+// 3.8 ms at 32 heads and 5.4 ms at 16.
 static bool use_pp(const dcp_attn_desc_t* d) {
   const long long elt = d->kv_dtype == DCP_BF16 ? 2 : 1;
   static_assert(PP<false>::kMaxTiles >= 8192 / kT && PP<true>::kMaxTiles >= 8192 / kT,
                 "a window holds one block of the largest size");
-  return desc_rows(d) >= 64 && d->block_size % kT == 0 && d->block_size <= 8192 &&
+  const int rows = desc_rows(d);
+  return (rows >= 64 || (desc_q_len(d) == 1 && (rows == 16 || rows == 32))) &&
+         d->block_size % kT == 0 && d->block_size <= 8192 &&
          d->kv_token_stride * elt * kT < (1ll << 30) &&
          d->kv_block_stride * elt < (1ll << 32) &&
          d->kv_token_stride * elt * d->block_size < (1ll << 32) &&
@@ -1998,7 +2012,7 @@ hipError_t launch_mla(const AttnLaunch& L, hipStream_t stream) {
   const int heads = a.Hq < 64 ? a.Hq : 64;
   const dim3 grid(kGroups, a.Hq / heads);
   if (mla_sequence_pieces(d, L.scale_ts)) {
-    const int ngrp = a.Hq / 64;
+    const int ngrp = a.Hq >= 64 ? a.Hq / 64 : 1;  // 16 or 32 rows: one padded group
     const dim3 pgrid(kGroups * ngrp);
     if (ngrp > 1) {
       if (fp8)

@@ -136,3 +136,33 @@ def test_empty_cache_pool():
     o, lse = dcp.decode_all_shards(desc, dev.q, None, None, None, dev.block_table, dev.seq_lens)
     torch.cuda.synchronize()
     assert float(o.abs().max()) == 0.0 and bool((lse == -np.inf).all())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("hq", [16, 32])
+def test_latent_few_heads_padded_group(dtype, hq):
+    """Single-token latent decode with 16 or 32 query heads runs as one 64-row
+    head group padded with zero queries: the results of the real heads match
+    the oracle, and nothing is written past the workspace (a guard zone after
+    it keeps its fill)."""
+    lens = [0, 1, 63, 64, 65, 1000, 4097, 9000, 2, 300]
+    w = _workload("mla", dtype, 64, 4, hq, 1, 576, lens, seed=17)
+    dev = W.to_torch(w)
+    desc = desc_for(w, dev)
+    n = dcp.workspace_size(desc)
+    guard = 1 << 20
+    buf = torch.full((n + guard,), 0x5A, dtype=torch.uint8, device=dev.q.device)
+    o, lse = dcp.decode_all_shards(desc, dev.q, dev.k_cache, dev.v_cache, dev.kv_scale,
+                                   dev.block_table, dev.seq_lens, workspace=buf[:n])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_reference(w)
+    compare(o, lse, o_ref, lse_ref, **TOL[dtype], label=f"all shards {hq} heads")
+    assert bool((buf[n:] == 0x5A).all()), "write past the workspace"
+    lt, ll = dcp.block_remap(dev.block_table, dev.seq_lens, 64, 4)
+    opr, lpr = oracle.shard_partials(w)
+    for r in range(4):
+        o_r, l_r = dcp.decode_partial(desc, dev.q, dev.k_cache, dev.v_cache, dev.kv_scale,
+                                      lt[r].contiguous(), ll[r].contiguous(), workspace=buf[:n])
+        torch.cuda.synchronize()
+        compare(o_r, l_r, opr[r], lpr[r], **TOL[dtype], label=f"shard {r} {hq} heads")
+    assert bool((buf[n:] == 0x5A).all()), "write past the workspace"

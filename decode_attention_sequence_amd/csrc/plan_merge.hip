@@ -75,6 +75,18 @@ __device__ __forceinline__ int split_start(int total_c, int G, int g) {
   return static_cast<int>(static_cast<long long>(total_c) * g / G);
 }
 
+// The range holding cost position y (0 <= y < total_c): the last g in [0, G)
+// with split_start(g) <= y, in closed form. Whole units: g * cc <= y. Shares:
+// floor(total_c * g / G) <= y exactly when total_c * g < (y + 1) * G.
+__device__ __forceinline__ int range_at(int total_c, int G, int y) {
+  if (total_c < 8 * G) {
+    const int cc = max(1, (total_c + G - 1) / G);
+    return min(G - 1, y / cc);
+  }
+  const long long g = ((static_cast<long long>(y) + 1) * G - 1) / total_c;
+  return static_cast<int>(min(static_cast<long long>(G - 1), g));
+}
+
 __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int seg_cost, int Hq,
                                                     int seq_pieces, PlanHeader* hdr, int32_t* seg_off,
                                                     int32_t* cost_off, int32_t* wg_start,
@@ -85,7 +97,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
   __shared__ int l_seg[kPlanLds];
   __shared__ int l_cost[kPlanLds];
   __shared__ int l_wg[kPlanLds];
-  __shared__ int l_sc[kPlanLds];  // split_start of each range
   const bool mirror_s = S + 1 <= kPlanLds;
   const bool mirror_g = G + 1 <= kPlanLds;
   const int t = threadIdx.x;
@@ -157,7 +168,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
   // few units per segment, so 32-bit arithmetic suffices.)
   for (int g = t; g <= G; g += 1024) {
     const int y = split_start(total_c, G, g);
-    if (mirror_g) l_sc[g] = y;
     // last segment s < S with cost_off[s] <= y
     int lo = 0, hi = S;
     while (hi - lo > 1) {
@@ -179,16 +189,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(SegMap m, int S, int G, int 
   // The work group of block i of segment s is the range holding its cost
   // position cost_off[s] + seg_cost + i (the same split as above): the last g
   // with start(g) <= that position.
-  __syncthreads();  // wg_start and the split starts complete
-  auto range_of = [&](unsigned y) {
-    int lo = 0, hi = G;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      const int st = mirror_g ? l_sc[mid] : split_start(total_c, G, mid);
-      if (static_cast<unsigned>(st) <= y) lo = mid; else hi = mid;
-    }
-    return lo;
-  };
+  __syncthreads();  // wg_start complete
+  auto range_of = [&](unsigned y) { return range_at(total_c, G, static_cast<int>(y)); };
   if (seq_pieces) {
     // One partial per work group and sequence: sequence b's blocks (contiguous
     // over its segments) lie in work groups g0..g1, whose partials sit in slots

@@ -18,6 +18,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 #define DCP_LDS __attribute__((address_space(3)))
 
@@ -72,7 +73,9 @@ __device__ __forceinline__ bool plan_matches(const PlanSig& want, const PlanHead
 // Workspace layout: PlanHeader, seg_off[S + 1], cost_off[S + 1],
 // wg_start[G + 1], seq_slots[B][2], wg_seg[G + 1] and lens[B] (int32), then at
 // 256-byte alignment lse slots [num_slots, Hq] fp32, then o slots [num_slots,
-// Hq, v_dim] fp32.
+// Hq, v_dim] fp32. Sequence pieces (the latent producer/consumer kernel) fill
+// only the first half of each row: v_dim fp16 values, each kPieceSlice-column
+// slice scaled by a power of two, then the slices' scales (fp32).
 
 struct SegMap {
   const int32_t* table;  // [B, width]
@@ -219,6 +222,9 @@ struct WorkspaceView {
   float* o;
   int num_slots;
 };
+
+// Columns of a sequence piece's row that share one scale: a value wave's slice.
+constexpr int kPieceSlice = 128;
 
 // Partial slots of a launch: one per (work group, segment) piece, S + G - 1;
 // with sequence pieces (one partial per work group and sequence), B + G - 1.

@@ -196,6 +196,13 @@ __device__ __forceinline__ float vmax_xor32(float x) {
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// The largest of |a|, |b|, |c| (operand modifiers on v_max3).
+__device__ __forceinline__ float vmax3_abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // A value every lane holds identically, moved to a scalar register.
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -1017,6 +1024,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufWord3);
 }
 
+// Stores one head's value slice of a finished sequence piece and restarts its
+// accumulators: the slice's kPieceSlice columns lie on the head's 4 lanes q4
+// (lanes 16 apart), kMT tiles of 4 columns on each. The values are normalised
+// by inv and multiplied by the power of two 2^-e that puts the slice's largest
+// magnitude in [0.5, 1), then rounded to fp16 (nearest even, relative error
+// at most 2^-11 of that largest magnitude); 2^e goes to the slice's scale,
+// which the merge multiplies back. Half the bytes of fp32 rows, for the
+// attention kernel's stores and the merge's loads alike.
+template <int kMT>
+__device__ __forceinline__ void store_piece_f16(const MlaArgs& a, size_t slot, int head, int vbase,
+                                                int q4, f32x4* st, int nt, float inv, bool real) {
+  float mx = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) {
+    const f32x4 v = st[4 * mt + nt];
+    mx = vmax3_abs(mx, v[0], v[1]);
+    mx = vmax3_abs(mx, v[2], v[3]);
+  }
+  mx = vmax_xor32(vmax_xor16(mx));
+  const int e = __builtin_amdgcn_frexp_expf(mx * inv);  // (0 for an all-zero slice)
+  const float down = __builtin_amdgcn_ldexpf(inv, -e);
+  // (The row's first half: kV fp16 values, then the slices' scales.)
+  float* row = a.ws_o + (slot * a.Hq + head) * kV;
+  uint16_t* orow = reinterpret_cast<uint16_t*>(row) + vbase + 4 * q4;
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) {
+    if (real)
+      *reinterpret_cast<i32x2*>(orow + 16 * mt) =
+          __builtin_bit_cast(i32x2, __builtin_convertvector(st[4 * mt + nt] * down, f16x4));
+    st[4 * mt + nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (real && q4 == 0) row[kV / 2 + vbase / kPieceSlice] = __builtin_amdgcn_ldexpf(1.f, e);
+}
+
 // SHARED: several head groups (more than 64 query rows per sequence) stream
 // the same tiles. Their work groups run side by side on one XCD and the copies
 // keep the default cache policy, so the second group finds the tiles in L2.
@@ -1684,13 +1725,8 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
             for (int nt = 0; nt < 4; ++nt) {
               const float lt = __int_as_float(h0[nt]) + __int_as_float(h1[nt]);
               const float inv = lt > 0.f ? 1.f / lt : 0.f;
-              float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
               const bool real = head0 + 16 * nt < a.Hq;  // (rows past 16 or 32 query rows)
-#pragma unroll
-              for (int mt = 0; mt < P::kMT; ++mt) {
-                if (real) *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
-                st[4 * mt + nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-              }
+              store_piece_f16<P::kMT>(a, slot, head0 + 16 * nt + l16, vbase, q4, st, nt, inv, real);
               if (real && grp == 0 && q4 == 0)
                 a.ws_lse[slot * a.Hq + head0 + 16 * nt + l16] =
                     lt > 0.f ? (__int_as_float(mm[nt]) + fast_log2(lt)) * kLn2 : -INFINITY;
@@ -1903,13 +1939,8 @@ __global__ __launch_bounds__(512) void mla_pp_kernel(MlaArgs a) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
               const float inv = lt[nt] > 0.f ? 1.f / lt[nt] : 0.f;
-              float* orow = a.ws_o + (slot * a.Hq + head0 + 16 * nt + l16) * kV + vbase + 4 * q4;
               const bool real = head0 + 16 * nt < a.Hq;  // (rows past 16 or 32 query rows)
-#pragma unroll
-              for (int mt = 0; mt < P::kMT; ++mt) {
-                if (real) *reinterpret_cast<f32x4*>(orow + 16 * mt) = st[4 * mt + nt] * inv;
-                st[4 * mt + nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-              }
+              store_piece_f16<P::kMT>(a, slot, head0 + 16 * nt + l16, vbase, q4, st, nt, inv, real);
             }
             ++nfin;
           }

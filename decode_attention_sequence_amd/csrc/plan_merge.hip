@@ -311,7 +311,10 @@ __host__ __device__ inline int merge_heads(int v_dim) {
   return tph >= kMergeThreads ? 1 : kMergeThreads / tph;
 }
 
-template <class Src>
+// kF16: each row holds v_dim fp16 values in its first half, every
+// kPieceSlice-column slice scaled by a power of two stored after them
+// (sequence pieces); the slice's scale weights the row's contribution.
+template <class Src, bool kF16>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     Src src, const float* __restrict__ o_rows, const float* __restrict__ lse_rows, int H,
     int v_dim, void* out, int out_bf16, float* lse_out) {
@@ -337,20 +340,35 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   const int n = src.count(b);
   const int f0 = src.first(b);
   const float* orow = o_rows + static_cast<size_t>(h) * v_dim + 4 * v4;
+  const float* row = o_rows + static_cast<size_t>(h) * v_dim;
+  const uint16_t* orow16 = reinterpret_cast<const uint16_t*>(row) + 4 * v4;
+  const float* srow = row + v_dim / 2 + (4 * v4) / kPieceSlice;
   float m = -INFINITY;  // largest LSE so far
   float wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < n; k0 += kMergeRows) {
     f32x4 o[kMergeRows];
+    i32x2 o16[kMergeRows];  // (fp16 rows, widened at use)
     float l[kMergeRows];
+    float sc[kMergeRows];  // (fp16 rows) the row slice's scale
 #pragma unroll
     for (int u = 0; u < kMergeRows; ++u) {
       l[u] = -INFINITY;
-      o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kF16) {
+        o16[u] = i32x2{0, 0};
+        sc[u] = 1.f;
+      } else {
+        o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
       if (k0 + u < n) {
         const size_t slot = static_cast<size_t>(src.slot(b, k0 + u, f0));
         l[u] = lse_rows[slot * H + h];
-        o[u] = *reinterpret_cast<const f32x4*>(orow + slot * H * v_dim);
+        if constexpr (kF16) {
+          o16[u] = *reinterpret_cast<const i32x2*>(orow16 + 2 * slot * H * v_dim);
+          sc[u] = srow[slot * H * v_dim];
+        } else {
+          o[u] = *reinterpret_cast<const f32x4*>(orow + slot * H * v_dim);
+        }
       }
     }
     float mr = m;
@@ -371,8 +389,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
       const bool on = l[u] != -INFINITY;
       const float w = on ? fast_exp2(l[u] * kLog2e - ml) : 0.f;
       wsum += w;
+      f32x4 ou;
+      if constexpr (kF16) ou = __builtin_convertvector(__builtin_bit_cast(f16x4, o16[u]), f32x4);
+      else ou = o[u];
+      const float ws = kF16 ? w * sc[u] : w;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] += on ? w * o[u][c] : 0.f;
+      for (int c = 0; c < 4; ++c) acc[c] += on ? ws * ou[c] : 0.f;
     }
   }
   if (m != -INFINITY) acc *= 1.0f / wsum;
@@ -395,9 +417,12 @@ hipError_t launch_merge_pieces(const SegMap& m, const WorkspaceView& ws, const P
   PieceSource src{ws.seq_slots, ws.header, sig};
   const int hpb = merge_heads(v_dim);
   dim3 grid((Hq + hpb - 1) / hpb, m.batch);
-  hipLaunchKernelGGL(merge_kernel<PieceSource>, grid, dim3(kMergeThreads), 0, stream,
-                     src, ws.o, ws.lse, Hq,
-                     v_dim, out, out_dtype == DCP_BF16 ? 1 : 0, lse_out);
+  if (sig.seq_pieces)
+    hipLaunchKernelGGL((merge_kernel<PieceSource, true>), grid, dim3(kMergeThreads), 0, stream,
+                       src, ws.o, ws.lse, Hq, v_dim, out, out_dtype == DCP_BF16 ? 1 : 0, lse_out);
+  else
+    hipLaunchKernelGGL((merge_kernel<PieceSource, false>), grid, dim3(kMergeThreads), 0, stream,
+                       src, ws.o, ws.lse, Hq, v_dim, out, out_dtype == DCP_BF16 ? 1 : 0, lse_out);
   return hipGetLastError();
 }
 
@@ -407,9 +432,8 @@ hipError_t launch_merge_partials(const float* o, const float* lse, int P, int B,
   PartialSource src{P, B};
   const int hpb = merge_heads(v_dim);
   dim3 grid((H + hpb - 1) / hpb, B);
-  hipLaunchKernelGGL(merge_kernel<PartialSource>, grid, dim3(kMergeThreads), 0, stream,
-                     src, o, lse, H, v_dim,
-                     out, out_dtype == DCP_BF16 ? 1 : 0, lse_out);
+  hipLaunchKernelGGL((merge_kernel<PartialSource, false>), grid, dim3(kMergeThreads), 0, stream,
+                     src, o, lse, H, v_dim, out, out_dtype == DCP_BF16 ? 1 : 0, lse_out);
   return hipGetLastError();
 }
 

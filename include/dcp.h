@@ -121,7 +121,11 @@ typedef struct {
  *     tile's probability-times-scale weights are brought into fp16's range by
  *     exact powers of two, so the query may hold any finite values and the
  *     token scales any finite non-negative values up to 2^64 (nonzero scales
- *     below 2^-64 keep less than fp16 precision in their weights).
+ *     below 2^-64 keep less than fp16 precision in their weights). Where a
+ *     sequence is split between work groups, the latent kernels hand their
+ *     partial outputs to the merge as fp16, each 128-column slice scaled by a
+ *     power of two (at most 2^-11 of the slice's largest magnitude per value);
+ *     the merge and every output stay fp32.
  * Cache rows (the qk_dim / v_dim values of one token and head) must start on
  * a 16-byte boundary. */
 

@@ -1027,9 +1027,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, in
 // Stores one head's value slice of a finished sequence piece and restarts its
 // accumulators: the slice's kPieceSlice columns lie on the head's 4 lanes q4
 // (lanes 16 apart), kMT tiles of 4 columns on each. The values are normalised
-// by inv and multiplied by the power of two 2^-e that puts the slice's largest
-// magnitude in [0.5, 1), then rounded to fp16 (nearest even, relative error
-// at most 2^-11 of that largest magnitude); 2^e goes to the slice's scale,
+// by inv, then multiplied by the power of two that puts the slice's largest
+// magnitude in [2^14, 2^15), and rounded to fp16 (nearest even: at most 2^-11
+// of that largest magnitude); the inverse power of two, a normal fp32 number
+// for any finite slice (the exponent is clamped), goes to the slice's scale,
 // which the merge multiplies back. Half the bytes of fp32 rows, for the
 // attention kernel's stores and the merge's loads alike.
 template <int kMT>
@@ -1043,8 +1044,9 @@ __device__ __forceinline__ void store_piece_f16(const MlaArgs& a, size_t slot, i
     mx = vmax3_abs(mx, v[2], v[3]);
   }
   mx = vmax_xor32(vmax_xor16(mx));
-  const int e = __builtin_amdgcn_frexp_expf(mx * inv);  // (0 for an all-zero slice)
-  const float down = __builtin_amdgcn_ldexpf(inv, -e);
+  // mx * inv = f * 2^e with f in [0.5, 1) (e = 0 for an all-zero slice).
+  const int e = min(max(__builtin_amdgcn_frexp_expf(mx * inv), -100), 128);
+  const float up = __builtin_amdgcn_ldexpf(1.f, 15 - e);  // in [2^-113, 2^115]
   // (The row's first half: kV fp16 values, then the slices' scales.)
   float* row = a.ws_o + (slot * a.Hq + head) * kV;
   uint16_t* orow = reinterpret_cast<uint16_t*>(row) + vbase + 4 * q4;
@@ -1052,10 +1054,10 @@ __device__ __forceinline__ void store_piece_f16(const MlaArgs& a, size_t slot, i
   for (int mt = 0; mt < kMT; ++mt) {
     if (real)
       *reinterpret_cast<i32x2*>(orow + 16 * mt) =
-          __builtin_bit_cast(i32x2, __builtin_convertvector(st[4 * mt + nt] * down, f16x4));
+          __builtin_bit_cast(i32x2, __builtin_convertvector(st[4 * mt + nt] * inv * up, f16x4));
     st[4 * mt + nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  if (real && q4 == 0) row[kV / 2 + vbase / kPieceSlice] = __builtin_amdgcn_ldexpf(1.f, e);
+  if (real && q4 == 0) row[kV / 2 + vbase / kPieceSlice] = __builtin_amdgcn_ldexpf(1.f, e - 15);
 }
 
 // SHARED: several head groups (more than 64 query rows per sequence) stream

@@ -166,3 +166,35 @@ def test_latent_few_heads_padded_group(dtype, hq):
         torch.cuda.synchronize()
         compare(o_r, l_r, opr[r], lpr[r], **TOL[dtype], label=f"shard {r} {hq} heads")
     assert bool((buf[n:] == 0x5A).all()), "write past the workspace"
+
+
+def _scale_bf16_bits(x, k):
+    """bf16 bit patterns times 2^k, exactly (the exponent field moved by k);
+    zeros stay zero."""
+    e = ((x >> 7) & 0xFF).astype(np.int32)
+    assert e.max() + k < 255 and (e[e != 0].min() + k) > 0
+    y = x.astype(np.int32)
+    y[e != 0] += k << 7
+    return y.astype(np.uint16)
+
+
+@pytest.mark.parametrize("shift", [60, -60])
+def test_latent_piece_rows_far_outside_fp16_range(shift):
+    """A latent cache 2^shift times a normal draw, read by a query 2^-shift
+    times one: the scores, the softmax and the LSE are those of the unscaled
+    draw, and the outputs 2^shift times theirs, far outside fp16's range. The
+    fp16 partial rows of split sequences carry a power-of-two scale per
+    128-column slice, so the outputs match the oracle in relative terms."""
+    from dataclasses import replace
+
+    lens = [5000, 3000, 64, 1, 9000, 700]
+    w = _workload("mla", "bf16", 64, 4, 64, 1, 576, lens, seed=21)
+    w = replace(w, k_cache=_scale_bf16_bits(w.k_cache, shift), q=_scale_bf16_bits(w.q, -shift))
+    o_ref, lse_ref = oracle.decode_reference(w)
+    f = 2.0 ** -shift
+    o, lse, dev, _ = run_all_shards(w)
+    compare(o * f, lse, o_ref * f, lse_ref, **TOL["bf16"], label=f"all shards, 2^{shift}")
+    op, lp, _, _ = run_per_shard(w, dev)
+    opr, lpr = oracle.shard_partials(w)
+    for r in range(4):
+        compare(op[r] * f, lp[r], opr[r] * f, lpr[r], **TOL["bf16"], label=f"shard {r}, 2^{shift}")

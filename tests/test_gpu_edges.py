@@ -198,3 +198,19 @@ def test_latent_piece_rows_far_outside_fp16_range(shift):
     opr, lpr = oracle.shard_partials(w)
     for r in range(4):
         compare(op[r] * f, lp[r], opr[r] * f, lpr[r], **TOL["bf16"], label=f"shard {r}, 2^{shift}")
+
+
+@pytest.mark.parametrize("bs", [8224, 16384])
+def test_latent_blocks_above_8192_tokens(bs):
+    """Blocks of more than 8192 tokens (the producer/consumer kernel's window
+    holds at most one such block, so these go to the general latent kernel):
+    several blocks per sequence, a partial last block and an empty sequence."""
+    lens = [20000, bs + 1, 1, 0, 40000]
+    w = _workload("mla", "bf16", bs, 3, 64, 1, 576, lens, seed=23)
+    o_ref, lse_ref = oracle.decode_reference(w)
+    o, lse, dev, _ = run_all_shards(w)
+    compare(o, lse, o_ref, lse_ref, **TOL["bf16"], label=f"all shards, bs {bs}")
+    op, lp, _, _ = run_per_shard(w, dev)
+    opr, lpr = oracle.shard_partials(w)
+    for r in range(3):
+        compare(op[r], lp[r], opr[r], lpr[r], **TOL["bf16"], label=f"shard {r}, bs {bs}")

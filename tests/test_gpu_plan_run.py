@@ -28,6 +28,11 @@ SPECS = [
     W.scaled(W.SPECS["mla_bf16_b64_bimodal"]),     # B 8, ragged lengths, D 8
     W.scaled(W.SPECS["mla_fp8_b128_bimodal"]),     # B 16, ragged, fp8 + scales
 ]
+# Single-token latent decode with 16 or 32 heads (one zero-padded 64-row group).
+FEW_HEADS = [
+    replace(W.scaled(W.SPECS["mla_bf16_b64_bimodal"]), name="mla_bf16_16_heads", num_q_heads=16),
+    replace(W.scaled(W.SPECS["mla_fp8_b128_bimodal"]), name="mla_fp8_32_heads", num_q_heads=32),
+]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -54,7 +59,7 @@ def same(a, b):
     return torch.equal(a, b)
 
 
-@pytest.mark.parametrize("spec", SPECS, ids=lambda s: s.name)
+@pytest.mark.parametrize("spec", SPECS + FEW_HEADS, ids=lambda s: s.name)
 def test_partial_runs_on_one_plan_match_unplanned(spec):
     w = W.make(spec)
     dev = W.to_torch(w)
@@ -162,7 +167,8 @@ def test_run_without_a_matching_plan_writes_nan():
 
 
 @pytest.mark.parametrize("spec", [W.scaled(W.SPECS["mla_bf16_b64_bimodal"], 16, 128),
-                                  W.scaled(W.SPECS["gqa_bf16_b32_L32k"], 8, 64)],
+                                  W.scaled(W.SPECS["gqa_bf16_b32_L32k"], 8, 64),
+                                  FEW_HEADS[1]],
                          ids=lambda s: s.name)
 def test_run_captured_in_a_graph_follows_each_new_plan(spec):
     """The run alone captured in a HIP graph, the plan made eagerly before each

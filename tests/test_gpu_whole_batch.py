@@ -22,9 +22,11 @@ from gpu_helpers import TOL, compare, need_gpu
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-# (workload, query tokens per sequence)
-CASES = [("mla_bf16_b64_bimodal", 1), ("mla_fp8_b128_bimodal", 1), ("mla_fp8_b128_bimodal", 2),
-         ("gqa_bf16_b32_L32k", 1), ("mla_bf16_b8_L1m", 1)]
+# (workload, query tokens per sequence, query heads if not the workload's)
+CASES = [("mla_bf16_b64_bimodal", 1, None), ("mla_bf16_b64_bimodal", 1, 16),
+         ("mla_fp8_b128_bimodal", 1, None),
+         ("mla_fp8_b128_bimodal", 2, None),
+         ("gqa_bf16_b32_L32k", 1, None), ("mla_bf16_b8_L1m", 1, None)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -32,9 +34,12 @@ def _gpu():
     need_gpu()
 
 
-@pytest.mark.parametrize("name,q_len", CASES, ids=[f"{n}-q{q}" for n, q in CASES])
-def test_every_sequence(name, q_len):
+@pytest.mark.parametrize("name,q_len,heads", CASES,
+                         ids=[f"{n}-q{q}" + (f"-h{h}" if h else "") for n, q, h in CASES])
+def test_every_sequence(name, q_len, heads):
     spec = replace(W.SPECS[name], q_len=q_len)
+    if heads:
+        spec = replace(spec, num_q_heads=heads)
     w = W.make(spec)
     dev = W.to_torch(w, "cuda")
     kind = dcp.KV_LATENT if spec.kind == "mla" else dcp.KV_SEPARATE
@@ -46,7 +51,7 @@ def test_every_sequence(name, q_len):
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.decode_reference(w)
     stats = compare(o, lse, o_ref, lse_ref, **TOL[spec.kv_dtype], label=f"{name} q{q_len}")
-    print(f"\nwhole batch {name} q_len={q_len}: {spec.batch} sequences, "
+    print(f"\nwhole batch {name} q_len={q_len} heads={spec.num_q_heads}: {spec.batch} sequences, "
           f"{int(w.seq_lens.sum())} tokens: rel L2 {stats['rel_l2']:.3e}, worst sequence rel L2 "
           f"{stats['worst_seq_rel_l2']:.3e}, max |dO| {stats['max_abs']:.3e}, "
           f"max |dLSE| {stats['lse_abs']:.3e}", flush=True)

@@ -181,6 +181,18 @@ def components(dcp, desc, dev, w, ws, iters: int = 20):
         run_ms[r] = timed(lambda: dcp.decode_partial_run(
             desc, dev.q, dev.k_cache, dev.v_cache, dev.kv_scale, ltr, ws_plan,
             o_partial=o_parts[r], lse_partial=lse_parts[r]))
+    # Token-level ownership (position t on shard t % D): shard 0's partial read
+    # in place from the global table, every D-th row of each block.
+    lens_h = dev.seq_lens.cpu().numpy().astype(np.int64)
+    tok_bytes = int(((lens_h + D - 1) // D).sum()) * per_token
+    try:
+        tok_ms = timed(lambda: dcp.decode_partial_token(
+            desc, 0, dev.q, dev.k_cache, dev.v_cache, dev.kv_scale, dev.block_table, dev.seq_lens,
+            workspace=ws, o_partial=o_parts[0], lse_partial=lse_parts[0]))
+        token0 = {"shard": 0, "ms": round(tok_ms, 4), "kv_bytes": tok_bytes,
+                  "GBps": round(tok_bytes / (tok_ms * 1e-3) / 1e9, 1)}
+    except dcp.DcpValueError:  # (blocks not a multiple of D tokens)
+        token0 = None
     dcp.decode_all_shards_plan(desc, dev.seq_lens, ws_plan)
     fused_out = torch.empty((spec.batch, spec.num_q_heads, spec.v_dim),
                             dtype=torch.float32 if desc.out_dtype == dcp.F32 else torch.bfloat16,
@@ -218,7 +230,8 @@ def components(dcp, desc, dev, w, ws, iters: int = 20):
         "note": ("per call, wall time of back-to-back calls; each dcp_decode_partial includes its own "
                  "plan and piece merge; the *_run entries run on a plan made once before them "
                  "(dcp_decode_partial_plan / dcp_decode_all_shards_plan), as every layer of a "
-                 "decode step can"),
+                 "decode step can; decode_partial_token_shard0 is shard 0 under token-level "
+                 "ownership (its plan included)"),
         "block_remap_ms": round(remap_ms, 4),
         "block_remap_update_ms": round(upd_ms, 4),
         "kv_append_ms": round(append_ms, 4),
@@ -226,6 +239,7 @@ def components(dcp, desc, dev, w, ws, iters: int = 20):
         "decode_partial_slowest": shard(slow),
         "decode_partial_run_shard0": shard(0, run_ms[0]),
         "decode_partial_run_slowest": shard(slow, run_ms[slow]),
+        "decode_partial_token_shard0": token0,
         "decode_all_shards_run": {"ms": round(fused_run_ms, 4), "kv_bytes": fused_bytes,
                                   "GBps": round(fused_bytes / (fused_run_ms * 1e-3) / 1e9, 1)},
         "lse_merge": {"partials": D, "ms": round(merge_ms, 4), "bytes": merge_bytes,
